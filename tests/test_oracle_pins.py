@@ -1,0 +1,330 @@
+"""Pins of the fp64 oracle against facts fixed by mathematics, not by itself.
+
+The pages print no worked numbers, so every pin is a closed form, a hand
+derivation, a brute-force enumeration, an independent library routine or an
+invariant that the definitions imply. Each block names the mistake it would
+catch.
+"""
+import itertools
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+from synth import bf16_bits_to_f32, rne_bf16
+
+
+def bf(x):
+    return rne_bf16(np.asarray(x, dtype=np.float32))
+
+
+def exact_bf(x):
+    b = bf(x)
+    assert np.array_equal(bf16_bits_to_f32(b), np.asarray(x, np.float32)), "value not bf16-exact"
+    return b
+
+
+# ----------------------------------------------------------------- confidence
+
+def test_confidence_zero_weight_closed_form():
+    # w = 0 gives z = bias and p_i = sigma(bias / T_i). With bias = ln 9 and
+    # T = (1, 2, 4): sigma(ln x) = x / (1 + x) gives 9/10, 3/4, sqrt3/(1+sqrt3).
+    # Catches: temperature applied to w.h only (bias undivided), sign flip,
+    # dropped bias.
+    g, d = 3, 5
+    bias = np.float32(math.log(9.0))
+    h = bf(np.random.default_rng(1).standard_normal((2, g, d)))
+    w = exact_bf(np.zeros(d))
+    temps = np.array([1.0, 2.0, 4.0], np.float32)
+    z, p = oracle.confidence(h, w, bias, temps)
+    xb = math.exp(float(bias))                     # 9 up to the fp32 rounding of ln 9
+    want = [xb / (1 + xb), math.sqrt(xb) / (1 + math.sqrt(xb)), xb ** 0.25 / (1 + xb ** 0.25)]
+    for b in range(2):
+        assert np.allclose(p[b], want, rtol=0, atol=1e-14)
+        assert np.all(z[b] == float(bias))
+    assert abs(want[0] - 0.9) < 1e-7 and abs(want[1] - 0.75) < 1e-7
+
+
+def test_confidence_one_hot_picks_the_right_entry():
+    # h[b,i,:] = 2 * e_{k(b,i)} with distinct k per (b, i): z must equal
+    # 2 * w[k(b,i)] + bias exactly. Catches transposed or mis-strided hidden
+    # indexing and reading the wrong weight entry.
+    B, g, d = 3, 4, 16
+    rng = np.random.default_rng(2)
+    w_val = bf16_bits_to_f32(bf(rng.standard_normal(d)))
+    w = exact_bf(w_val)
+    hv = np.zeros((B, g, d), np.float32)
+    assert B * g <= d
+    for idx, (b, i) in enumerate(itertools.product(range(B), range(g))):
+        hv[b, i, (idx * 5) % d] = 2.0             # 5 is coprime to 16: distinct entries
+    h = exact_bf(hv)
+    bias = np.float32(-0.25)
+    temps = (1 + 0.5 * np.arange(g)).astype(np.float32)
+    z, p = oracle.confidence(h, w, bias, temps)
+    for b in range(B):
+        for i in range(g):
+            k = int(np.nonzero(hv[b, i])[0][0])
+            assert z[b, i] == 2.0 * float(w_val[k]) + float(bias)
+            # logit (inverse sigmoid) of p, times T_i, recovers z
+            assert abs(math.log(p[b, i] / (1 - p[b, i])) * temps[i] - z[b, i]) < 1e-12
+
+
+def test_confidence_matches_library_dot():
+    # numpy's float64 matmul is an independent dot product.
+    rng = np.random.default_rng(3)
+    B, g, d = 5, 7, 333
+    h = bf(rng.standard_normal((B, g, d)))
+    w = bf(rng.standard_normal(d) / math.sqrt(d))
+    bias = np.float32(0.125)
+    temps = (1 + 0.05 * np.arange(g)).astype(np.float32)
+    z, p = oracle.confidence(h, w, bias, temps)
+    zl = bf16_bits_to_f32(h).astype(np.float64) @ bf16_bits_to_f32(w).astype(np.float64) + 0.125
+    assert np.allclose(z, zl, rtol=0, atol=1e-12)
+    # log-odds identity, independent of how p was formed
+    assert np.allclose(np.log(p / (1 - p)) * temps[None, :], zl, rtol=0, atol=1e-9)
+
+
+def test_confidence_symmetry():
+    # With bias 0, negating h negates z, so p(h) + p(-h) = 1.
+    rng = np.random.default_rng(4)
+    hv = bf16_bits_to_f32(bf(rng.standard_normal((2, 6, 64))))
+    w = bf(rng.standard_normal(64) / 8)
+    temps = (1 + 0.1 * np.arange(6)).astype(np.float32)
+    _, p1 = oracle.confidence(exact_bf(hv), w, 0.0, temps)
+    _, p2 = oracle.confidence(exact_bf(-hv), w, 0.0, temps)
+    assert np.allclose(p1 + p2, 1.0, rtol=0, atol=1e-15)
+
+
+def test_confidence_rejects_bad_temperature():
+    h = bf(np.ones((1, 2, 4)))
+    w = bf(np.ones(4))
+    with pytest.raises(oracle.OracleError):
+        oracle.confidence(h, w, 0.0, np.array([1.0, 0.0], np.float32))
+
+
+# ------------------------------------------------------------------- survival
+
+def test_survival_constant_closed_form():
+    # constant p = 1/2 gives S_k = 2^-k exactly; catches an S_0 = 1 shift
+    # (which would give 2^-(k-1)).
+    s = oracle.survival(np.full((3, 10), 0.5))
+    assert np.array_equal(s, np.broadcast_to(0.5 ** np.arange(1, 11), (3, 10)))
+
+
+def test_survival_hand_example():
+    # p = (0.5, 0.25, 1, 0.8): S = (0.5, 0.125, 0.125, 0.1), by hand.
+    s = oracle.survival(np.array([[0.5, 0.25, 1.0, 0.8]]))
+    assert np.allclose(s, [[0.5, 0.125, 0.125, 0.1]], rtol=0, atol=1e-16)
+
+
+def test_survival_invariants_and_log_identity():
+    rng = np.random.default_rng(5)
+    p = rng.uniform(0, 1, (20, 16))
+    s = oracle.survival(p)
+    assert np.all(np.diff(s, axis=1) <= 0) and np.all(s >= 0) and np.all(s <= 1)
+    assert np.allclose(np.log(s), np.cumsum(np.log(p), axis=1), rtol=0, atol=1e-12)
+
+
+# ---------------------------------------------------------------- threshold
+
+def test_threshold_constant_closed_form():
+    # S_k = p^k: L = max{k <= gamma : p^k >= c} = min(gamma, floor(ln c / ln p)),
+    # with (p, c) chosen away from the boundary.
+    g = 16
+    for p, c in [(0.9, 0.5), (0.5, 0.3), (0.99, 0.01), (0.7, 0.69), (0.2, 0.3)]:
+        s = oracle.survival(np.full((1, g), p))
+        L = oracle.cut_threshold(s, np.array([c], np.float32))
+        want = min(g, math.floor(math.log(float(np.float32(c))) / math.log(p)))
+        assert L[0] == want, (p, c, L[0], want)
+
+
+def test_threshold_special_cases():
+    s = oracle.survival(np.array([[0.5, 0.5, 0.5]]))    # S = 0.5, 0.25, 0.125
+    cut = lambda c: int(oracle.cut_threshold(s, np.array([c], np.float32))[0])
+    assert cut(0.0) == 3 and cut(-1.0) == 3             # c <= 0 keeps everything
+    assert cut(1.5) == 0                                 # c > 1 keeps nothing
+    assert cut(float("nan")) == 0                        # NaN keeps nothing
+    assert cut(0.25) == 2                                # a tie is kept (>=)
+    assert cut(0.2500001) == 1
+
+
+def test_threshold_is_prefix_count():
+    rng = np.random.default_rng(6)
+    s = oracle.survival(rng.uniform(0.3, 1, (50, 16)))
+    c = rng.uniform(0, 1, 50).astype(np.float32)
+    L = oracle.cut_threshold(s, c)
+    for b in range(50):
+        keep = s[b] >= float(c[b])
+        assert L[b] == keep.sum()
+        assert np.all(keep[: L[b]]) and not np.any(keep[L[b]:])
+
+
+# ------------------------------------------------------------------- budget
+
+def _brute_force_budget(s, T):
+    B, g = s.shape
+    t_eff = min(T, B * g)
+    best, arg, nbest = -1.0, None, 0
+    for L in itertools.product(range(g + 1), repeat=B):
+        if sum(L) != t_eff:
+            continue
+        val = sum(s[b, :L[b]].sum() for b in range(B))
+        if val > best + 1e-12:
+            best, arg, nbest = val, L, 1
+        elif abs(val - best) <= 1e-12:
+            nbest += 1
+    return best, arg, nbest
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_budget_brute_force(seed):
+    # The top-T pick maximises the expected verified-and-surviving mass
+    # sum_b sum_{k<=L_b} S_k over all length vectors of total T (S is
+    # non-increasing, so prefix sums are concave). Enumerate every vector.
+    rng = np.random.default_rng(100 + seed)
+    B = int(rng.integers(1, 5))
+    g = int(rng.integers(1, 9 if B <= 3 else 7))
+    s = oracle.survival(rng.uniform(0.2, 1.0, (B, g)))
+    for T in sorted({0, 1, int(rng.integers(0, B * g + 1)), B * g // 2, B * g, B * g + 3}):
+        L = oracle.cut_budget(s, T)
+        best, arg, nbest = _brute_force_budget(s, T)
+        got = sum(s[b, :L[b]].sum() for b in range(B))
+        assert abs(got - best) <= 1e-12
+        assert L.sum() == min(T, B * g)
+        if nbest == 1:
+            assert tuple(L) == arg
+
+
+def test_budget_all_equal_ties_go_to_lower_requests():
+    s = np.full((3, 4), 0.5)
+    assert list(oracle.cut_budget(s, 6)) == [4, 2, 0]
+    assert list(oracle.cut_budget(s, 0)) == [0, 0, 0]
+    assert list(oracle.cut_budget(s, 12)) == [4, 4, 4]
+    assert list(oracle.cut_budget(s, 99)) == [4, 4, 4]
+
+
+def test_budget_hand_examples():
+    # S rows (0.9, 0.5) and (0.9, 0.6): ranking (0.9,b0), (0.9,b1), (0.6,b1), (0.5,b0)
+    s = np.array([[0.9, 0.5], [0.9, 0.6]])
+    assert list(oracle.cut_budget(s, 1)) == [1, 0]
+    assert list(oracle.cut_budget(s, 2)) == [1, 1]
+    assert list(oracle.cut_budget(s, 3)) == [1, 2]
+    s = np.array([[0.9, 0.6], [0.9, 0.6]])
+    assert list(oracle.cut_budget(s, 3)) == [2, 1]
+
+
+def test_budget_rejects_negative():
+    with pytest.raises(oracle.OracleError):
+        oracle.cut_budget(np.full((1, 2), 0.5), -1)
+
+
+# ------------------------------------------------------------------ compact
+
+def test_compact_against_library_scan():
+    rng = np.random.default_rng(7)
+    B, g = 37, 9
+    L = rng.integers(0, g + 1, B).astype(np.int32)
+    tok = rng.integers(0, 50000, (B, g + 1)).astype(np.int32)
+    cu, pt, ps = oracle.compact(L, tok)
+    assert np.array_equal(cu, np.concatenate([[0], np.cumsum(L + 1)]))
+    total = int((L + 1).sum())
+    assert np.array_equal(pt[:total], np.concatenate([tok[b, :L[b] + 1] for b in range(B)]))
+    dense = np.concatenate([b * (g + 1) + np.arange(L[b] + 1) for b in range(B)])
+    assert np.array_equal(ps[:total], dense)
+    assert np.all(np.diff(ps[:total]) > 0)
+    assert np.all(pt[total:] == -1) and np.all(ps[total:] == -1)   # tail untouched
+
+
+def test_compact_rejects_bad_length():
+    with pytest.raises(oracle.OracleError):
+        oracle.compact(np.array([3], np.int32), np.zeros((1, 3), np.int32))
+
+
+# ------------------------------------------------------------------- argmax
+
+def test_argmax_matches_library_first_occurrence():
+    rng = np.random.default_rng(8)
+    rows = bf(rng.standard_normal((40, 777)) * 2)
+    rows[5, 100] = rows[5, 3] = bf([50.0])[0]          # exact tie: lowest index wins
+    rows[6, :] = bf(1.0)                          # all equal -> index 0
+    am = oracle.argmax_rows(rows)
+    assert np.array_equal(am, np.argmax(bf16_bits_to_f32(rows), axis=1))
+    assert am[5] == 3 and am[6] == 0
+
+
+def test_argmax_signed_zero_and_negatives():
+    rows = np.stack([exact_bf([-0.0, 0.0, -1.0]), exact_bf([-3.0, -0.0, 0.0]),
+                     exact_bf([-5.0, -2.0, -2.0])])
+    assert list(oracle.argmax_rows(rows)) == [0, 1, 1]
+
+
+def test_argmax_src_rows_and_nonfinite():
+    rng = np.random.default_rng(9)
+    rows = bf(rng.standard_normal((10, 64)))
+    src = np.array([7, 2, 2, 9], np.int32)
+    assert np.array_equal(oracle.argmax_rows(rows, src), oracle.argmax_rows(rows)[src])
+    rows[3, 5] = 0x7FC0                            # NaN is rejected
+    with pytest.raises(oracle.OracleError):
+        oracle.argmax_rows(rows, np.array([3], np.int32))
+
+
+# ------------------------------------------------------------- accept/bonus
+
+@pytest.mark.parametrize("seed", range(6))
+def test_accept_known_planted_prefix(seed):
+    # Every row's argmax is known by construction (one entry at +50 in a row
+    # of values in [-2, 2]); drafts agree with the rows for exactly m_b
+    # positions. Then a_b = min(L_b, m_b) and bonus_b = the known argmax of
+    # row a_b. Catches off-by-one between rows and drafts and a missing cap.
+    rng = np.random.default_rng(200 + seed)
+    B, g, V = 6, 7, 300
+    L = rng.integers(0, g + 1, B).astype(np.int32)
+    m = rng.integers(0, g + 1, B)
+    top = rng.integers(0, V, (B, g + 1))                 # argmax of dense row (b, j)
+    logits = rng.uniform(-2, 2, (B, g + 1, V)).astype(np.float32)
+    for b in range(B):
+        for j in range(g + 1):
+            logits[b, j, top[b, j]] = 50.0
+    tok = np.zeros((B, g + 1), np.int32)
+    tok[:, 0] = rng.integers(0, V, B)
+    for b in range(B):
+        for j in range(g):
+            tok[b, j + 1] = top[b, j] if j < m[b] else (top[b, j] + 1 + rng.integers(0, V - 1)) % V
+    lg = bf(logits)
+    cu, pt, ps = oracle.compact(L, tok)
+    am = oracle.argmax_rows(lg.reshape(-1, V), ps[: cu[-1]])
+    acc, bon = oracle.accept(cu, tok, am)
+    for b in range(B):
+        a = min(int(L[b]), int(m[b]))
+        assert acc[b] == a
+        assert bon[b] == top[b, a]
+        if a < L[b]:
+            assert bon[b] != tok[b, a + 1]
+
+
+# --------------------------------------------------------------- whole step
+
+def test_step_equals_stage_chain_and_invariants():
+    rng = np.random.default_rng(10)
+    B, g, d, V = 9, 6, 48, 200
+    h = bf(rng.standard_normal((B, g, d)))
+    w = bf(rng.standard_normal(d) / math.sqrt(d))
+    temps = (1 + 0.05 * np.arange(g)).astype(np.float32)
+    tok = rng.integers(0, V, (B, g + 1)).astype(np.int32)
+    lg = bf(rng.standard_normal((B, g + 1, V)))
+    c = rng.uniform(0.05, 0.6, B).astype(np.float32)
+    for mode in ("threshold", "budget"):
+        o = oracle.step(h, w, 0.3, temps, tok, lg, mode, cutoff=c, budget=17)
+        z, p = oracle.confidence(h, w, 0.3, temps)
+        s = oracle.survival(p)
+        L = oracle.cut_threshold(s, c) if mode == "threshold" else oracle.cut_budget(s, 17)
+        cu, pt, ps = oracle.compact(L, tok)
+        am = oracle.argmax_rows(lg.reshape(-1, V), ps[: cu[-1]])
+        acc, bon = oracle.accept(cu, tok, am)
+        assert np.array_equal(o["lengths"], L) and np.array_equal(o["cu_seqlens"], cu)
+        assert np.array_equal(o["packed_argmax"][: cu[-1]], am)
+        assert np.array_equal(o["accepted"], acc) and np.array_equal(o["bonus"], bon)
+        assert np.all(acc <= L) and cu[-1] == (L + 1).sum()
+        if mode == "budget":
+            assert L.sum() == 17
