@@ -1,0 +1,265 @@
+#!/usr/bin/env python3
+"""Benchmark of the fused verify step (dspark_step) on one MI355X.
+
+Workload: mixed traffic, B=256 requests, gamma=16 drafted tokens, drafter
+hidden d=4096 (bf16), target vocabulary V=151936 (bf16 logits), half the
+requests predictable and half prose-like, per-request cutoff c=0.25. The same
+seeded inputs are also run under the batch budget T=742 (2.9 per request), and
+the budget workload with d=7168, V=129280, T=768 is reported beside it.
+
+A step is one dspark_step call over one batch. R distinct seeded batches
+(each with its own 1.3 GB dense logit block) stay resident in HBM and are
+cycled, so consecutive steps never re-read cached rows. W warm-up steps run
+untimed; then K steps are timed between two device synchronisations, with a
+pair of HIP events (on the stream the kernels are launched on) around each
+step. One JSON line goes to stdout; progress goes to stderr.
+
+Reported:
+  value        packed verify rows per second (sum of cu_seqlens[B] over the
+               K steps / elapsed time)
+  roofline     algorithmic bytes of one step / mean step time against the
+               8 TB/s HBM peak
+  cpu_baseline the fp64 oracle's whole step on the host (one thread) on a
+               bounded sample of the same batches, in the same unit
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def step_bytes(cfg, total: int) -> int:
+    """Algorithmic HBM bytes of one step: every input the method must read once
+    and every output it writes, with the logits counted only at packed rows."""
+    B, g, d, V = cfg.B, cfg.gamma, cfg.d, cfg.V
+    reads = (2 * B * g * d            # hidden states
+             + 2 * d + 4 * g          # head weight, temperatures
+             + (4 * B if cfg.mode == "threshold" else 0)   # cutoffs
+             + 4 * B * (g + 1)        # verify-block tokens
+             + 2 * V * total)         # packed logit rows
+    writes = (8 * B * g               # conf, survival
+              + 4 * B + 4 * (B + 1)   # lengths, cu_seqlens
+              + 12 * total            # packed tokens, source rows, argmax
+              + 8 * B)                # accepted, bonus
+    return reads + writes
+
+
+def run_arm(cfg, slots, outs, ws, steps, warmup, dspark, torch):
+    """Time `steps` dspark_step calls cycling over the resident slots."""
+    R = len(slots)
+
+    def launch(i):
+        s = slots[i % R]
+        dspark.dspark_step(s.hidden, s.w, s.bias, s.temps, s.tokens, s.logits, cfg.mode,
+                           cutoff=s.cutoff, budget=cfg.budget, out=outs[i % R], ws=ws)
+
+    for i in range(warmup):
+        launch(i)
+    torch.cuda.synchronize()
+    totals = [int(o["cu_seqlens"][-1].item()) for o in outs]
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        ev[i][0].record()
+        launch(i)
+        ev[i][1].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    step_ms = [a.elapsed_time(b) for a, b in ev]
+    rows = sum(totals[i % R] for i in range(steps))
+    nbytes = sum(step_bytes(cfg, totals[i % R]) for i in range(steps))
+    mean_ms = sum(step_ms) / steps
+    return dict(wall_s=wall, rows=rows, bytes=nbytes, mean_step_ms=mean_ms,
+                step_ms_sorted=sorted(step_ms), totals=totals)
+
+
+def arm_summary(cfg, r, steps, B):
+    ev_s = r["mean_step_ms"] * steps / 1e3
+    return dict(
+        rows_per_s=r["rows"] / r["wall_s"],
+        request_steps_per_s=B * steps / r["wall_s"],
+        ms_per_step=r["wall_s"] * 1e3 / steps,
+        event_ms_per_step=r["mean_step_ms"],
+        p10_ms=r["step_ms_sorted"][len(r["step_ms_sorted"]) // 10],
+        p90_ms=r["step_ms_sorted"][(9 * len(r["step_ms_sorted"])) // 10],
+        mean_packed_rows=r["rows"] / steps,
+        achieved_gbs=r["bytes"] / ev_s / 1e9,
+        frac_of_hbm_peak=r["bytes"] / ev_s / 1e9 / HBM_PEAK_GBS,
+    )
+
+
+def cpu_baseline(cfg, slots, min_s=10.0, max_s=30.0):
+    """The oracle's whole step, single-threaded, on the first batches of the
+    rotation until at least `min_s` seconds of CPU work (capped at `max_s`)."""
+    import numpy as np
+
+    import oracle
+
+    host = []
+    for s in slots[:2]:
+        host.append(dict(hidden=s.host("hidden"), w=s.host("w"), temps=s.host("temps"),
+                         tokens=s.host("tokens"), cutoff=s.host("cutoff"),
+                         logits=s.host("logits"), bias=s.bias, budget=s.budget))
+    rows = 0
+    n = 0
+    results = []
+    t0 = time.perf_counter()
+    while True:
+        h = host[n % len(host)]
+        o = oracle.step(h["hidden"], h["w"], h["bias"], h["temps"], h["tokens"], h["logits"],
+                        cfg.mode, cutoff=h["cutoff"], budget=h["budget"])
+        if n < len(host):
+            results.append(o)
+        rows += int(o["cu_seqlens"][-1])
+        n += 1
+        el = time.perf_counter() - t0
+        if el >= min_s or el >= max_s:
+            break
+    for s in slots[:2]:
+        s._host.pop("logits", None)
+    del np
+    return dict(value=rows / el, unit="packed verify rows/s", cores=1, kind="oracle",
+                sample=f"{n} whole steps (batches 0-{len(host) - 1} of the rotation, "
+                       f"{rows} packed rows) of the same workload in {el:.1f} s",
+                seconds=el), results
+
+
+def check_against_oracle(results, outs):
+    """Integer outputs of the GPU's own runs of the sampled batches against the
+    oracle's results on those batches (exact); conf/survival within 1e-5."""
+    import numpy as np
+
+    ok = True
+    for o, g in zip(results, outs):
+        gg = {k: v.cpu().numpy() for k, v in g.items()}
+        total = int(o["cu_seqlens"][-1])
+        ok &= bool(np.max(np.abs(gg["conf"] - o["conf"])) <= 1e-5)
+        ok &= bool(np.max(np.abs(gg["survival"] - o["survival"])) <= 1e-5)
+        for k in ("lengths", "cu_seqlens", "accepted", "bonus"):
+            ok &= bool(np.array_equal(gg[k], o[k]))
+        for k in ("packed_tokens", "packed_src_row", "packed_argmax"):
+            ok &= bool(np.array_equal(gg[k][:total], o[k][:total]))
+    return ok
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--rotation", type=int, default=8)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extra-arms", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: the verify hot path runs on a single MI355X here "
+              f"and --gpus {args.gpus} is not supported", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import confidence_scheduled_ragged_amd as dspark
+    from synth import CONFIGS, make_params, make_step
+
+    dev = torch.device("cuda:0")
+    dspark.lib()
+    cfg_t = CONFIGS["mixed_threshold"]
+    cfg_b = CONFIGS["mixed_budget"]
+    params = make_params(cfg_t)
+    log(f"generating {args.rotation} resident batches of B={cfg_t.B} gamma={cfg_t.gamma} "
+        f"d={cfg_t.d} V={cfg_t.V}")
+    slots = []
+    for i in range(args.rotation):
+        slots.append(make_step(cfg_t, i, device=dev, params=params))
+    torch.cuda.synchronize()
+    log("batches resident")
+    ws = dspark.workspace(cfg_t.B, cfg_t.gamma, cfg_t.V, dev)
+    outs = [dspark.alloc_step_outputs(cfg_t.B, cfg_t.gamma, dev) for _ in slots]
+
+    r_t = run_arm(cfg_t, slots, outs, ws, args.steps, args.warmup, dspark, torch)
+    s_t = arm_summary(cfg_t, r_t, args.steps, cfg_t.B)
+    log(f"threshold arm: {s_t['rows_per_s']:.3e} rows/s, {s_t['event_ms_per_step'] * 1e3:.1f} us/step, "
+        f"{s_t['achieved_gbs']:.0f} GB/s ({100 * s_t['frac_of_hbm_peak']:.1f} % of peak)")
+
+    extra = {}
+    cpu = None
+    parity = None
+    if not args.no_cpu_baseline:
+        log("timing the oracle on the host (bounded sample)")
+        cpu, results = cpu_baseline(cfg_t, slots)
+        # the GPU outputs of the first timed batches: rerun them once more to be sure the
+        # buffers hold exactly those batches' results
+        for i in range(len(results)):
+            s = slots[i]
+            dspark.dspark_step(s.hidden, s.w, s.bias, s.temps, s.tokens, s.logits, cfg_t.mode,
+                               cutoff=s.cutoff, budget=s.budget, out=outs[i], ws=ws)
+        torch.cuda.synchronize()
+        parity = check_against_oracle(results, outs[: len(results)])
+        cpu.pop("seconds", None)
+        log(f"oracle: {cpu['value']:.1f} rows/s on 1 core; parity on sampled batches: {parity}")
+
+    if not args.no_extra_arms:
+        # budget arm on the same resident batches (the two arms share their seeds)
+        r_b = run_arm(cfg_b, slots, outs, ws, args.steps, args.warmup, dspark, torch)
+        extra["mixed_budget_T742"] = arm_summary(cfg_b, r_b, args.steps, cfg_b.B)
+        log(f"budget arm: {extra['mixed_budget_T742']['rows_per_s']:.3e} rows/s")
+        del slots, outs
+        torch.cuda.empty_cache()
+        cfg4 = CONFIGS["budget"]
+        p4 = make_params(cfg4)
+        slots4 = [make_step(cfg4, i, device=dev, params=p4) for i in range(args.rotation)]
+        outs4 = [dspark.alloc_step_outputs(cfg4.B, cfg4.gamma, dev) for _ in slots4]
+        ws4 = dspark.workspace(cfg4.B, cfg4.gamma, cfg4.V, dev)
+        r_4 = run_arm(cfg4, slots4, outs4, ws4, args.steps, args.warmup, dspark, torch)
+        extra["budget_d7168_V129280_T768"] = arm_summary(cfg4, r_4, args.steps, cfg4.B)
+        log(f"budget d=7168 arm: {extra['budget_d7168_V129280_T768']['rows_per_s']:.3e} rows/s")
+
+    mean_bytes = r_t["bytes"] / args.steps
+    line = {
+        "metric": "packed verify rows/s + achieved HBM GB/s (frac of peak), B=256 gamma=16 V=151936",
+        "value": s_t["rows_per_s"],
+        "unit": "packed verify rows/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": s_t["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "mixed traffic: B=256 gamma=16 d=4096 V=151936, half predictable "
+                               "half prose-like, per-request cutoff c=0.25, fused dspark_step",
+                   "B": cfg_t.B, "gamma": cfg_t.gamma, "d": cfg_t.d, "V": cfg_t.V,
+                   "mode": "threshold", "rotation": args.rotation,
+                   "mean_packed_rows": s_t["mean_packed_rows"]},
+        "request_steps_per_s": s_t["request_steps_per_s"],
+        "achieved_gbs": s_t["achieved_gbs"],
+        "roofline": {"bound": "hbm", "kernel": "dspark_step",
+                     "achieved": mean_bytes / (r_t["mean_step_ms"] / 1e3) / 1e9,
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": mean_bytes / (r_t["mean_step_ms"] / 1e3) / 1e9 / HBM_PEAK_GBS,
+                     "traffic": None,
+                     "algorithmic_bytes_per_launch": mean_bytes,
+                     "mean_launch_us": r_t["mean_step_ms"] * 1e3},
+        "cpu_baseline": cpu,
+        "parity_on_sampled_batches": parity,
+        "arms": extra,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,289 @@
+"""Python binding of libdspark, the MI355X verify hot path (argument marshalling only).
+
+Every function here has the name of a C entry point declared in
+``include/dspark.h`` and does nothing but check that tensors are on the GPU
+with the expected dtype and layout, allocate missing outputs with torch, and
+pass raw device pointers plus torch's current HIP stream to the library. All
+computation happens in the HIP kernels of ``libdspark.so``; there is no CPU
+fallback, and every entry point raises ImportError when the library is not
+built.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Dict, Optional
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libdspark.so")
+
+DSPARK_CUT_THRESHOLD = 0
+DSPARK_CUT_BUDGET = 1
+MODES = {"threshold": DSPARK_CUT_THRESHOLD, "budget": DSPARK_CUT_BUDGET}
+
+_lib = None
+
+
+class DsparkError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        msg = lib().dspark_status_string(status).decode()
+        super().__init__(f"{fn}: status {status} ({msg})")
+        self.status = status
+
+
+def lib() -> ctypes.CDLL:
+    """Load libdspark.so (built in-tree); raise if it is missing."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(
+                f"{LIB_PATH} is not built; run `python -m confidence_scheduled_ragged_amd.build` "
+                "or `python -c 'import __graft_entry__; __graft_entry__.build()'`")
+        L = ctypes.CDLL(LIB_PATH)
+        P, I, F, LL, S = (ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_longlong,
+                          ctypes.c_size_t)
+        L.dspark_confidence.argtypes = [P, P, F, P, I, I, I, P, P, P]
+        L.dspark_schedule.argtypes = [P, I, I, I, P, LL, P, P]
+        L.dspark_compact.argtypes = [P, P, I, I, P, P, P, P, I, P, P]
+        L.dspark_accept.argtypes = [P, P, P, P, I, I, I, P, P, P, P, S, P]
+        L.dspark_step.argtypes = [P, P, F, P, P, P, I, I, I, I, I, P, LL, P, P, P, P, P, P, P, P,
+                                  P, P, S, P]
+        L.dspark_workspace_bytes.argtypes = [I, I, I]
+        L.dspark_workspace_bytes.restype = S
+        L.dspark_workspace_init.argtypes = [P, S, P]
+        L.dspark_status_string.argtypes = [I]
+        L.dspark_status_string.restype = ctypes.c_char_p
+        for f in (L.dspark_confidence, L.dspark_schedule, L.dspark_compact, L.dspark_accept,
+                  L.dspark_step, L.dspark_workspace_init):
+            f.restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+# ------------------------------------------------------------------ helpers
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _need(t: torch.Tensor, name: str, dtype: torch.dtype, shape=None) -> torch.Tensor:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be a GPU tensor (got {t.device})")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype} (got {t.dtype})")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)} (got {tuple(t.shape)})")
+    return t
+
+
+def _stream(device: torch.device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _ok(fn: str, status: int):
+    if status != 0:
+        raise DsparkError(fn, status)
+
+
+def _mode(mode) -> int:
+    return MODES[mode] if isinstance(mode, str) else int(mode)
+
+
+def dspark_status_string(status: int) -> str:
+    return lib().dspark_status_string(int(status)).decode()
+
+
+# --------------------------------------------------------------- workspace
+
+def dspark_workspace_bytes(B: int, gamma: int, V: int) -> int:
+    return int(lib().dspark_workspace_bytes(B, gamma, V))
+
+
+def dspark_workspace_init(ws: torch.Tensor) -> None:
+    _need(ws, "ws", torch.uint8)
+    _ok("dspark_workspace_init",
+        lib().dspark_workspace_init(_ptr(ws), ws.numel(), _stream(ws.device)))
+
+
+_WS: Dict[tuple, torch.Tensor] = {}
+
+
+def workspace(B: int, gamma: int, V: int, device) -> torch.Tensor:
+    """A zero-initialised workspace of the required size, cached per device.
+    Calls sharing it must not overlap in time (one stream, or ordered)."""
+    device = torch.device(device)
+    need = dspark_workspace_bytes(B, gamma, V)
+    if need == 0:
+        raise ValueError(f"invalid sizes B={B} gamma={gamma} V={V}")
+    key = (device.type, device.index)
+    ws = _WS.get(key)
+    if ws is None or ws.numel() < need:
+        ws = torch.empty(need, dtype=torch.uint8, device=device)
+        dspark_workspace_init(ws)
+        _WS[key] = ws
+    return ws
+
+
+# ------------------------------------------------------------- entry points
+
+def dspark_confidence(hidden, w, bias, temps, conf=None, survival=None):
+    """Steps 1-2: conf[b,i] and survival[b,i] ([B, gamma] fp32)."""
+    B, g, d = hidden.shape
+    _need(hidden, "hidden", torch.bfloat16)
+    _need(w, "w", torch.bfloat16, (d,))
+    _need(temps, "temps", torch.float32, (g,))
+    dev = hidden.device
+    conf = torch.empty((B, g), dtype=torch.float32, device=dev) if conf is None else conf
+    survival = torch.empty((B, g), dtype=torch.float32, device=dev) if survival is None else survival
+    _need(conf, "conf", torch.float32, (B, g))
+    _need(survival, "survival", torch.float32, (B, g))
+    _ok("dspark_confidence", lib().dspark_confidence(
+        _ptr(hidden), _ptr(w), float(bias), _ptr(temps), B, g, d, _ptr(conf), _ptr(survival),
+        _stream(dev)))
+    return conf, survival
+
+
+def dspark_schedule(survival, mode, cutoff=None, budget=0, lengths=None):
+    """Step 3: lengths[B] int32 from the survival curves."""
+    B, g = survival.shape
+    _need(survival, "survival", torch.float32)
+    m = _mode(mode)
+    if cutoff is not None:
+        _need(cutoff, "cutoff", torch.float32, (B,))
+    dev = survival.device
+    lengths = torch.empty(B, dtype=torch.int32, device=dev) if lengths is None else lengths
+    _need(lengths, "lengths", torch.int32, (B,))
+    _ok("dspark_schedule", lib().dspark_schedule(
+        _ptr(survival), B, g, m, _ptr(cutoff), int(budget), _ptr(lengths), _stream(dev)))
+    return lengths
+
+
+def dspark_compact(lengths, tokens, logits=None, out=None):
+    """Step 4: (cu_seqlens, packed_tokens, packed_src_row, packed_logits or None)."""
+    B, g1 = tokens.shape
+    g = g1 - 1
+    _need(lengths, "lengths", torch.int32, (B,))
+    _need(tokens, "tokens", torch.int32)
+    dev = tokens.device
+    cap = B * g1
+    out = out or {}
+    cu = out.get("cu_seqlens")
+    ptok = out.get("packed_tokens")
+    psrc = out.get("packed_src_row")
+    cu = torch.empty(B + 1, dtype=torch.int32, device=dev) if cu is None else cu
+    ptok = torch.full((cap,), -1, dtype=torch.int32, device=dev) if ptok is None else ptok
+    psrc = torch.full((cap,), -1, dtype=torch.int32, device=dev) if psrc is None else psrc
+    _need(cu, "cu_seqlens", torch.int32, (B + 1,))
+    _need(ptok, "packed_tokens", torch.int32, (cap,))
+    _need(psrc, "packed_src_row", torch.int32, (cap,))
+    plog = None
+    V = 0
+    if logits is not None:
+        _need(logits, "logits", torch.bfloat16)
+        V = logits.shape[-1]
+        if logits.numel() != cap * V:
+            raise ValueError("logits must hold B*(gamma+1) rows")
+        plog = out.get("packed_logits")
+        plog = torch.zeros((cap, V), dtype=torch.bfloat16, device=dev) if plog is None else plog
+        _need(plog, "packed_logits", torch.bfloat16, (cap, V))
+    _ok("dspark_compact", lib().dspark_compact(
+        _ptr(lengths), _ptr(tokens), B, g, _ptr(cu), _ptr(ptok), _ptr(psrc), _ptr(logits), V,
+        _ptr(plog), _stream(dev)))
+    return cu, ptok, psrc, plog
+
+
+def dspark_accept(logits, packed_src_row, cu_seqlens, tokens, out=None, ws=None):
+    """Steps 5-6: (packed_argmax, accepted, bonus). packed_src_row None means
+    `logits` is already packed ([B*(gamma+1), V], rows past cu_seqlens[B] unused)."""
+    B, g1 = tokens.shape
+    g = g1 - 1
+    _need(logits, "logits", torch.bfloat16)
+    V = logits.shape[-1]
+    _need(cu_seqlens, "cu_seqlens", torch.int32, (B + 1,))
+    _need(tokens, "tokens", torch.int32)
+    cap = B * g1
+    # dense [B*(gamma+1), V] with source rows, or packed rows with capacity
+    # B*(gamma+1) (the packed total is a device value, so the full capacity is
+    # required for the reads to stay inside the buffer)
+    if logits.numel() != cap * V:
+        raise ValueError("logits must hold B*(gamma+1) rows of V entries")
+    if packed_src_row is not None:
+        _need(packed_src_row, "packed_src_row", torch.int32, (cap,))
+    dev = tokens.device
+    out = out or {}
+    pam = out.get("packed_argmax")
+    acc = out.get("accepted")
+    bon = out.get("bonus")
+    pam = torch.full((cap,), -1, dtype=torch.int32, device=dev) if pam is None else pam
+    acc = torch.empty(B, dtype=torch.int32, device=dev) if acc is None else acc
+    bon = torch.empty(B, dtype=torch.int32, device=dev) if bon is None else bon
+    _need(pam, "packed_argmax", torch.int32, (cap,))
+    _need(acc, "accepted", torch.int32, (B,))
+    _need(bon, "bonus", torch.int32, (B,))
+    ws = workspace(B, g, V, dev) if ws is None else _need(ws, "ws", torch.uint8)
+    _ok("dspark_accept", lib().dspark_accept(
+        _ptr(logits), _ptr(packed_src_row), _ptr(cu_seqlens), _ptr(tokens), B, g, V, _ptr(pam),
+        _ptr(acc), _ptr(bon), _ptr(ws), ws.numel(), _stream(dev)))
+    return pam, acc, bon
+
+
+STEP_OUTPUTS = ("conf", "survival", "lengths", "cu_seqlens", "packed_tokens", "packed_src_row",
+                "packed_argmax", "accepted", "bonus")
+
+
+def alloc_step_outputs(B: int, gamma: int, device, with_conf: bool = True) -> Dict[str, torch.Tensor]:
+    cap = B * (gamma + 1)
+    i32 = dict(dtype=torch.int32, device=device)
+    out = dict(lengths=torch.empty(B, **i32), cu_seqlens=torch.empty(B + 1, **i32),
+               packed_tokens=torch.full((cap,), -1, **i32),
+               packed_src_row=torch.full((cap,), -1, **i32),
+               packed_argmax=torch.full((cap,), -1, **i32),
+               accepted=torch.empty(B, **i32), bonus=torch.empty(B, **i32))
+    if with_conf:
+        out["conf"] = torch.empty((B, gamma), dtype=torch.float32, device=device)
+        out["survival"] = torch.empty((B, gamma), dtype=torch.float32, device=device)
+    return out
+
+
+def dspark_step(hidden, w, bias, temps, tokens, logits, mode, cutoff=None, budget=0, out=None,
+                ws=None):
+    """Steps 1-6 in one call; returns the dict of output tensors."""
+    B, g, d = hidden.shape
+    V = logits.shape[-1]
+    _need(hidden, "hidden", torch.bfloat16)
+    _need(w, "w", torch.bfloat16, (d,))
+    _need(temps, "temps", torch.float32, (g,))
+    _need(tokens, "tokens", torch.int32, (B, g + 1))
+    _need(logits, "logits", torch.bfloat16, (B, g + 1, V))
+    m = _mode(mode)
+    if cutoff is not None:
+        _need(cutoff, "cutoff", torch.float32, (B,))
+    dev = hidden.device
+    out = alloc_step_outputs(B, g, dev) if out is None else out
+    cap = B * (g + 1)
+    shapes = dict(conf=(B, g), survival=(B, g), lengths=(B,), cu_seqlens=(B + 1,),
+                  packed_tokens=(cap,), packed_src_row=(cap,), packed_argmax=(cap,),
+                  accepted=(B,), bonus=(B,))
+    for k, shp in shapes.items():
+        if out.get(k) is not None:
+            _need(out[k], k, torch.float32 if k in ("conf", "survival") else torch.int32, shp)
+    ws = workspace(B, g, V, dev) if ws is None else _need(ws, "ws", torch.uint8)
+    _ok("dspark_step", lib().dspark_step(
+        _ptr(hidden), _ptr(w), float(bias), _ptr(temps), _ptr(tokens), _ptr(logits), B, g, d, V,
+        m, _ptr(cutoff), int(budget), _ptr(out.get("conf")), _ptr(out.get("survival")),
+        _ptr(out["lengths"]), _ptr(out["cu_seqlens"]), _ptr(out["packed_tokens"]),
+        _ptr(out["packed_src_row"]), _ptr(out["packed_argmax"]), _ptr(out["accepted"]),
+        _ptr(out["bonus"]), _ptr(ws), ws.numel(), _stream(dev)))
+    return out
+
+
+__all__ = ["DsparkError", "lib", "LIB_PATH", "dspark_status_string", "dspark_confidence", "dspark_schedule",
+           "dspark_compact", "dspark_accept", "dspark_step", "dspark_workspace_bytes",
+           "dspark_workspace_init", "workspace", "alloc_step_outputs", "STEP_OUTPUTS",
+           "DSPARK_CUT_THRESHOLD", "DSPARK_CUT_BUDGET"]

@@ -1,0 +1,162 @@
+// argmax_dev.hpp - greedy target choice over packed verify rows, acceptance
+// and bonus token, as device functions shared by the stage kernels and the
+// fused step kernel.
+//
+// [P1] "DFlash to DSpark in SGLang", section "Background": the target checks
+// the drafted tokens in one forward, the agreeing prefix is committed, and
+// the forward yields one extra (bonus) token. Greedy verification takes the
+// largest logit of each row, the lowest index among equal maxima.
+#pragma once
+
+#include "common.hpp"
+
+namespace dspark {
+
+// Fold eight consecutive bf16 logits (one 16-byte slot starting at element
+// `base`) into a lane's running (best, bidx). A slot only replaces the best
+// when its maximum is strictly larger, and inside the slot the first element
+// equal to that maximum is taken, so each lane keeps the first maximum of the
+// elements it has seen in increasing order.
+__device__ __forceinline__ void fold_slot(u32x4 a, int base, float &best, int &bidx) {
+    const float x0 = bf16_lo(a[0]), x1 = bf16_hi(a[0]), x2 = bf16_lo(a[1]), x3 = bf16_hi(a[1]);
+    const float x4 = bf16_lo(a[2]), x5 = bf16_hi(a[2]), x6 = bf16_lo(a[3]), x7 = bf16_hi(a[3]);
+    const float m = fmaxf(fmaxf(fmaxf(x0, x1), fmaxf(x2, x3)), fmaxf(fmaxf(x4, x5), fmaxf(x6, x7)));
+    if (m > best || bidx < 0) {
+        int j = 7;
+        j = (x6 == m) ? 6 : j;
+        j = (x5 == m) ? 5 : j;
+        j = (x4 == m) ? 4 : j;
+        j = (x3 == m) ? 3 : j;
+        j = (x2 == m) ? 2 : j;
+        j = (x1 == m) ? 1 : j;
+        j = (x0 == m) ? 0 : j;
+        best = m;
+        bidx = base + j;
+    }
+}
+
+// One lane's share of slots [v0, v1) of a row: slots v0+lane, v0+lane+64, ...
+// kVec: a slot is 8 bf16 (16-byte aligned row); otherwise a slot is one bf16.
+// kUnroll loads are issued before any is consumed.
+template <bool kVec, int kUnroll>
+__device__ __forceinline__ void lane_row_segment(const uint16_t *__restrict__ row, int64_t v0,
+                                                 int64_t v1, int lane, float &best, int &bidx) {
+    if (kVec) {
+        const u32x4 *r4 = reinterpret_cast<const u32x4 *>(row);
+        int64_t v = v0 + lane;
+        for (; v + (int64_t)(kUnroll - 1) * kWave < v1; v += (int64_t)kUnroll * kWave) {
+            u32x4 buf[kUnroll];
+#pragma unroll
+            for (int u = 0; u < kUnroll; ++u) buf[u] = __builtin_nontemporal_load(r4 + v + u * kWave);
+#pragma unroll
+            for (int u = 0; u < kUnroll; ++u) fold_slot(buf[u], (int)((v + u * kWave) * 8), best, bidx);
+        }
+        for (; v < v1; v += kWave) fold_slot(__builtin_nontemporal_load(r4 + v), (int)(v * 8), best, bidx);
+    } else {
+        for (int64_t v = v0 + lane; v < v1; v += kWave) {
+            const float x = bf16_f32(row[v]);
+            if (x > best || bidx < 0) {
+                best = x;
+                bidx = (int)v;
+            }
+        }
+    }
+}
+
+// Packed rows clamped to the capacity of the packed arrays.
+__device__ __forceinline__ int packed_total(const int32_t *cu, int B, int cap) {
+    int t = cu[B];
+    return t < 0 ? 0 : (t > cap ? cap : t);
+}
+
+// Argmax work of wave w of W over the packed rows (balanced partition, see
+// partition_q). Packed row r reads dense row psrc[r] (or row r when psrc is
+// NULL); a source row outside [0, cap) leaves key 0 ("no element").
+template <bool kVec, int kUnroll>
+__device__ __forceinline__ void wave_argmax_share(const uint16_t *__restrict__ logits,
+                                                  const int32_t *__restrict__ psrc, int total,
+                                                  int cap, int V, int64_t w, int64_t W,
+                                                  uint64_t *__restrict__ keys) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const int64_t Vv = kVec ? (V >> 3) : V;
+    const int64_t E = (int64_t)total * Vv;
+    const int64_t Q = partition_q(E, W);
+    int64_t e = w * Q;
+    if (e >= E) return;
+    const int64_t e_end = e + Q < E ? e + Q : E;
+    int64_t r = e / Vv;
+    while (e < e_end) {
+        const int64_t row_end = (r + 1) * Vv;
+        const int64_t seg_end = e_end < row_end ? e_end : row_end;
+        const int src = psrc ? psrc[r] : (int)r;
+        float best = -INFINITY;
+        int bidx = -1;
+        if (src >= 0 && src < cap) {
+            const uint16_t *row = logits + (size_t)src * (size_t)V;
+            lane_row_segment<kVec, kUnroll>(row, e - r * Vv, seg_end - r * Vv, lane, best, bidx);
+        }
+        uint64_t key = bidx >= 0 ? argmax_key(best, (uint32_t)bidx) : 0ull;
+        key = wave_max_u64(key);
+        if (lane == 0) keys[w + r] = key;
+        e = seg_end;
+        ++r;
+    }
+}
+
+// Argmax of packed row r from the keys of the waves whose shares touch it.
+__device__ __forceinline__ int32_t row_argmax(const uint64_t *__restrict__ keys, int64_t r,
+                                              int64_t Vv, int64_t Q) {
+    const int64_t w_lo = (r * Vv) / Q;
+    const int64_t w_hi = ((r + 1) * Vv - 1) / Q;
+    uint64_t k = 0;
+    for (int64_t w = w_lo; w <= w_hi; ++w) {
+        const uint64_t x = keys[w + r];
+        k = x > k ? x : k;
+    }
+    return key_index(k);
+}
+
+// Acceptance and bonus of request b by one wave: lane j handles packed row
+// cu[b] + j (chunks of 64 rows). The first row j where the target disagrees
+// with draft j+1, or j = L_b, is the accepted count; its argmax is the bonus.
+__device__ __forceinline__ void wave_accept_request(const uint64_t *__restrict__ keys,
+                                                    const int32_t *__restrict__ cu,
+                                                    const int32_t *__restrict__ tokens, int b,
+                                                    int gamma, int total, int64_t Vv, int64_t Q,
+                                                    int32_t *__restrict__ pam,
+                                                    int32_t *__restrict__ acc,
+                                                    int32_t *__restrict__ bonus) {
+    const int lane = threadIdx.x & (kWave - 1);
+    int start = cu[b], end = cu[b + 1];
+    start = start < 0 ? 0 : (start > total ? total : start);
+    end = end < start ? start : (end > total ? total : end);
+    const int n = end - start;
+    if (n <= 0) {
+        if (lane == 0) {
+            acc[b] = 0;
+            bonus[b] = -1;
+        }
+        return;
+    }
+    const int L = n - 1 < gamma ? n - 1 : gamma;
+    const int32_t *tok = tokens + (size_t)b * (gamma + 1);
+    int a = -1;
+    for (int j0 = 0; j0 < n; j0 += kWave) {
+        const int j = j0 + lane;
+        int32_t am = -1;
+        bool stop = false;
+        if (j < n) {
+            am = row_argmax(keys, start + j, Vv, Q);
+            pam[start + j] = am;
+            stop = (j >= L) || (am != tok[j + 1]);
+        }
+        const uint64_t mask = __ballot(stop);
+        if (a < 0 && mask != 0ull) a = j0 + __ffsll((unsigned long long)mask) - 1;
+    }
+    if (lane == 0) {
+        acc[b] = a;
+        bonus[b] = row_argmax(keys, start + a, Vv, Q);
+    }
+}
+
+}  // namespace dspark

@@ -1,0 +1,194 @@
+// capi.hip - the exported C ABI: host-side argument checks, then launches on
+// the caller's stream. No allocation, no synchronisation, no per-call state.
+#include <atomic>
+#include <cmath>
+
+#include "common.hpp"
+
+#define DSPARK_API extern "C" __attribute__((visibility("default")))
+
+namespace dspark {
+
+int device_cu_count() {
+    static std::atomic<int> cache[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) dev = 0;
+    if (dev >= 0 && dev < 64) {
+        int c = cache[dev].load(std::memory_order_relaxed);
+        if (c > 0) return c;
+    }
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        n <= 0)
+        n = 256;
+    if (dev >= 0 && dev < 64) cache[dev].store(n, std::memory_order_relaxed);
+    return n;
+}
+
+__global__ __launch_bounds__(256) void fill_zero_kernel(u32x4 *p, size_t n16) {
+    for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n16;
+         i += (size_t)gridDim.x * blockDim.x)
+        p[i] = u32x4{0u, 0u, 0u, 0u};
+}
+
+hipError_t launch_fill_zero(void *ws, size_t bytes, hipStream_t s) {
+    const size_t n16 = bytes / 16;
+    if (n16 == 0) return hipSuccess;
+    size_t g = (n16 + 255) / 256;
+    g = g > 1024 ? 1024 : g;
+    hipLaunchKernelGGL(fill_zero_kernel, dim3((unsigned)g), dim3(256), 0, s,
+                       static_cast<u32x4 *>(ws), n16);
+    return hipGetLastError();
+}
+
+}  // namespace dspark
+
+using namespace dspark;
+
+namespace {
+
+constexpr int kMaxD = 1 << 20;
+
+inline bool misaligned(const void *p, size_t a) { return p && ((uintptr_t)p % a) != 0; }
+
+inline dspark_status check_bg(int B, int gamma) {
+    if (B < 1 || gamma < 1 || gamma > DSPARK_MAX_GAMMA) return DSPARK_ERR_SHAPE;
+    if ((int64_t)B * (gamma + 1) > (int64_t)DSPARK_MAX_ROWS) return DSPARK_ERR_SHAPE;
+    return DSPARK_OK;
+}
+
+inline dspark_status launched(hipError_t e) { return e == hipSuccess ? DSPARK_OK : DSPARK_ERR_HIP; }
+
+inline hipStream_t as_stream(void *s) { return static_cast<hipStream_t>(s); }
+
+}  // namespace
+
+DSPARK_API const char *dspark_status_string(int status) {
+    switch (status) {
+        case DSPARK_OK: return "ok";
+        case DSPARK_ERR_NULL: return "a required pointer is NULL";
+        case DSPARK_ERR_SHAPE: return "a size is out of range";
+        case DSPARK_ERR_ARG: return "an argument value is invalid";
+        case DSPARK_ERR_ALIGN: return "a pointer is misaligned for its element type";
+        case DSPARK_ERR_WORKSPACE: return "the workspace is too small";
+        case DSPARK_ERR_HIP: return "a HIP kernel launch failed";
+        default: return "unknown status";
+    }
+}
+
+DSPARK_API size_t dspark_workspace_bytes(int B, int gamma, int V) {
+    if (check_bg(B, gamma) != DSPARK_OK || V < 1) return 0;
+    return ws_total_bytes(B, gamma);
+}
+
+DSPARK_API dspark_status dspark_workspace_init(void *ws, size_t ws_bytes, void *stream) {
+    if (!ws) return DSPARK_ERR_NULL;
+    if (misaligned(ws, 16)) return DSPARK_ERR_ALIGN;
+    return launched(launch_fill_zero(ws, ws_bytes & ~(size_t)15, as_stream(stream)));
+}
+
+DSPARK_API dspark_status dspark_confidence(const dspark_bf16 *hidden, const dspark_bf16 *w,
+                                           float bias, const float *temps, int B, int gamma, int d,
+                                           float *conf, float *survival, void *stream) {
+    if (!hidden || !w || !temps || !conf || !survival) return DSPARK_ERR_NULL;
+    if (dspark_status st = check_bg(B, gamma)) return st;
+    if (d < 1 || d > kMaxD) return DSPARK_ERR_SHAPE;
+    if (!std::isfinite(bias)) return DSPARK_ERR_ARG;
+    if (misaligned(hidden, 2) || misaligned(w, 2) || misaligned(temps, 4) || misaligned(conf, 4) ||
+        misaligned(survival, 4))
+        return DSPARK_ERR_ALIGN;
+    return launched(launch_confidence(hidden, w, bias, temps, B, gamma, d, conf, survival,
+                                      as_stream(stream)));
+}
+
+DSPARK_API dspark_status dspark_schedule(const float *survival, int B, int gamma, int mode,
+                                         const float *cutoff, long long budget, int32_t *lengths,
+                                         void *stream) {
+    if (!survival || !lengths) return DSPARK_ERR_NULL;
+    if (mode == DSPARK_CUT_THRESHOLD && !cutoff) return DSPARK_ERR_NULL;
+    if (dspark_status st = check_bg(B, gamma)) return st;
+    if (mode != DSPARK_CUT_THRESHOLD && mode != DSPARK_CUT_BUDGET) return DSPARK_ERR_ARG;
+    if (mode == DSPARK_CUT_BUDGET && budget < 0) return DSPARK_ERR_ARG;
+    if (misaligned(survival, 4) || misaligned(cutoff, 4) || misaligned(lengths, 4))
+        return DSPARK_ERR_ALIGN;
+    return launched(launch_schedule(survival, B, gamma, mode, cutoff, budget, lengths,
+                                    as_stream(stream)));
+}
+
+DSPARK_API dspark_status dspark_compact(const int32_t *lengths, const int32_t *tokens, int B,
+                                        int gamma, int32_t *cu_seqlens, int32_t *packed_tokens,
+                                        int32_t *packed_src_row, const dspark_bf16 *logits, int V,
+                                        dspark_bf16 *packed_logits, void *stream) {
+    if (!lengths || !tokens || !cu_seqlens || !packed_tokens || !packed_src_row)
+        return DSPARK_ERR_NULL;
+    if ((logits == nullptr) != (packed_logits == nullptr)) return DSPARK_ERR_NULL;
+    if (dspark_status st = check_bg(B, gamma)) return st;
+    if (logits && V < 1) return DSPARK_ERR_SHAPE;
+    if (misaligned(lengths, 4) || misaligned(tokens, 4) || misaligned(cu_seqlens, 4) ||
+        misaligned(packed_tokens, 4) || misaligned(packed_src_row, 4) || misaligned(logits, 2) ||
+        misaligned(packed_logits, 2))
+        return DSPARK_ERR_ALIGN;
+    hipStream_t s = as_stream(stream);
+    hipError_t e = launch_compact(lengths, tokens, B, gamma, cu_seqlens, packed_tokens,
+                                  packed_src_row, s);
+    if (e == hipSuccess && logits)
+        e = launch_gather_rows(logits, packed_src_row, cu_seqlens, B, gamma, V, packed_logits, s);
+    return launched(e);
+}
+
+DSPARK_API dspark_status dspark_accept(const dspark_bf16 *logits, const int32_t *packed_src_row,
+                                       const int32_t *cu_seqlens, const int32_t *tokens, int B,
+                                       int gamma, int V, int32_t *packed_argmax, int32_t *accepted,
+                                       int32_t *bonus, void *ws, size_t ws_bytes, void *stream) {
+    if (!logits || !cu_seqlens || !tokens || !packed_argmax || !accepted || !bonus || !ws)
+        return DSPARK_ERR_NULL;
+    if (dspark_status st = check_bg(B, gamma)) return st;
+    if (V < 1) return DSPARK_ERR_SHAPE;
+    if (misaligned(logits, 2) || misaligned(packed_src_row, 4) || misaligned(cu_seqlens, 4) ||
+        misaligned(tokens, 4) || misaligned(packed_argmax, 4) || misaligned(accepted, 4) ||
+        misaligned(bonus, 4) || misaligned(ws, 16))
+        return DSPARK_ERR_ALIGN;
+    if (ws_bytes < ws_total_bytes(B, gamma)) return DSPARK_ERR_WORKSPACE;
+    return launched(launch_accept(logits, packed_src_row, cu_seqlens, tokens, B, gamma, V,
+                                  packed_argmax, accepted, bonus, ws, as_stream(stream)));
+}
+
+DSPARK_API dspark_status dspark_step(const dspark_bf16 *hidden, const dspark_bf16 *w, float bias,
+                                     const float *temps, const int32_t *tokens,
+                                     const dspark_bf16 *logits, int B, int gamma, int d, int V,
+                                     int mode, const float *cutoff, long long budget, float *conf,
+                                     float *survival, int32_t *lengths, int32_t *cu_seqlens,
+                                     int32_t *packed_tokens, int32_t *packed_src_row,
+                                     int32_t *packed_argmax, int32_t *accepted, int32_t *bonus,
+                                     void *ws, size_t ws_bytes, void *stream) {
+    if (!hidden || !w || !temps || !tokens || !logits || !lengths || !cu_seqlens ||
+        !packed_tokens || !packed_src_row || !packed_argmax || !accepted || !bonus || !ws)
+        return DSPARK_ERR_NULL;
+    if (mode == DSPARK_CUT_THRESHOLD && !cutoff) return DSPARK_ERR_NULL;
+    if (dspark_status st = check_bg(B, gamma)) return st;
+    if (d < 1 || d > kMaxD || V < 1) return DSPARK_ERR_SHAPE;
+    if (mode != DSPARK_CUT_THRESHOLD && mode != DSPARK_CUT_BUDGET) return DSPARK_ERR_ARG;
+    if (mode == DSPARK_CUT_BUDGET && budget < 0) return DSPARK_ERR_ARG;
+    if (!std::isfinite(bias)) return DSPARK_ERR_ARG;
+    if (misaligned(hidden, 2) || misaligned(w, 2) || misaligned(temps, 4) ||
+        misaligned(tokens, 4) || misaligned(logits, 2) || misaligned(cutoff, 4) ||
+        misaligned(conf, 4) || misaligned(survival, 4) || misaligned(lengths, 4) ||
+        misaligned(cu_seqlens, 4) || misaligned(packed_tokens, 4) ||
+        misaligned(packed_src_row, 4) || misaligned(packed_argmax, 4) ||
+        misaligned(accepted, 4) || misaligned(bonus, 4) || misaligned(ws, 16))
+        return DSPARK_ERR_ALIGN;
+    if (ws_bytes < ws_total_bytes(B, gamma)) return DSPARK_ERR_WORKSPACE;
+    hipStream_t s = as_stream(stream);
+    char *wsb = static_cast<char *>(ws);
+    float *surv = survival ? survival
+                           : reinterpret_cast<float *>(wsb + ws_surv_offset((int64_t)B * (gamma + 1)));
+    float *cf = conf ? conf : reinterpret_cast<float *>(wsb + ws_conf_offset(B, gamma));
+    hipError_t e = launch_confidence(hidden, w, bias, temps, B, gamma, d, cf, surv, s);
+    if (e == hipSuccess) e = launch_schedule(surv, B, gamma, mode, cutoff, budget, lengths, s);
+    if (e == hipSuccess)
+        e = launch_compact(lengths, tokens, B, gamma, cu_seqlens, packed_tokens, packed_src_row, s);
+    if (e == hipSuccess)
+        e = launch_accept(logits, packed_src_row, cu_seqlens, tokens, B, gamma, V, packed_argmax,
+                          accepted, bonus, ws, s);
+    return launched(e);
+}

@@ -1,0 +1,116 @@
+// common.hpp - device helpers, workspace layout and internal launch prototypes
+// shared by the HIP kernels of the verify hot path (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "dspark.h"
+
+namespace dspark {
+
+constexpr int kWave = 64;
+
+// ---------------------------------------------------------------- bf16 lanes
+// A 32-bit word holds two bf16 values; the lower half is the lower index.
+__device__ __forceinline__ float bf16_lo(uint32_t u) { return __uint_as_float(u << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t u) { return __uint_as_float(u & 0xFFFF0000u); }
+__device__ __forceinline__ float bf16_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// ------------------------------------------------------------- argmax keys
+// A 64-bit key orders (value, index) pairs so that the larger key has the
+// larger value and, on equal values, the lower index: the high word is the
+// value's bits mapped to an order-preserving unsigned integer (with -0 folded
+// onto +0), the low word is the bitwise complement of the index. Key 0 means
+// "no element".
+__device__ __forceinline__ uint32_t ordered_bits(float v) {
+    uint32_t u = __float_as_uint(v);
+    if ((u & 0x7FFFFFFFu) == 0u) u = 0u;  // -0 -> +0
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ uint64_t argmax_key(float v, uint32_t idx) {
+    return ((uint64_t)ordered_bits(v) << 32) | (uint64_t)(0xFFFFFFFFu - idx);
+}
+__device__ __forceinline__ int32_t key_index(uint64_t k) {
+    return k == 0 ? -1 : (int32_t)(0xFFFFFFFFu - (uint32_t)k);
+}
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t k) {
+#pragma unroll
+    for (int off = kWave / 2; off > 0; off >>= 1) {
+        uint64_t o = __shfl_xor(k, off, kWave);
+        k = o > k ? o : k;
+    }
+    return k;
+}
+__device__ __forceinline__ float wave_sum_f32(float x) {
+    // Butterfly: partners add the same two values, so every lane ends with the
+    // same bit pattern and the order is fixed (deterministic).
+#pragma unroll
+    for (int off = kWave / 2; off > 0; off >>= 1) x += __shfl_xor(x, off, kWave);
+    return x;
+}
+
+// Inclusive scan of one int per lane across a wave.
+__device__ __forceinline__ int wave_incl_scan(int x, int lane) {
+#pragma unroll
+    for (int off = 1; off < kWave; off <<= 1) {
+        int y = __shfl_up(x, off, kWave);
+        if (lane >= off) x += y;
+    }
+    return x;
+}
+
+// ---------------------------------------------------- balanced row partition
+// The packed logit rows form one virtual array of total*Vv vector slots
+// (Vv = slots per row). Wave w of W owns slots [w*Q, min((w+1)*Q, E)),
+// E = total*Vv, Q = max(kMinSlotsPerWave, ceil(E/W)). The segment of wave w
+// inside packed row r stores its key at keys[w + r]: walking the array, each
+// row or wave boundary raises w + r by one, so these indices never collide.
+constexpr int64_t kMinSlotsPerWave = 64;
+
+__device__ __forceinline__ int64_t partition_q(int64_t E, int64_t W) {
+    int64_t q = (E + W - 1) / W;
+    return q < kMinSlotsPerWave ? kMinSlotsPerWave : q;
+}
+
+// ------------------------------------------------------------ workspace map
+// [0, 256)                          control words (fused step; self-cleaning)
+// [256, 256 + 8*(kMaxWaves + cap))   argmax segment keys (cap = B*(gamma+1))
+// then float [B*gamma]               survival scratch (when the caller passes none)
+// then float [B*gamma]               score scratch (when the caller passes none)
+constexpr int64_t kMaxWaves = 16384;
+constexpr size_t kCtrlBytes = 256;
+
+inline size_t ws_keys_offset() { return kCtrlBytes; }
+inline size_t ws_surv_offset(int64_t cap) {
+    return kCtrlBytes + (size_t)8 * (size_t)(kMaxWaves + cap);
+}
+inline size_t ws_conf_offset(int64_t B, int64_t gamma) {
+    return ws_surv_offset(B * (gamma + 1)) + (size_t)4 * (size_t)(B * gamma);
+}
+inline size_t ws_total_bytes(int64_t B, int64_t gamma) {
+    size_t s = ws_conf_offset(B, gamma) + (size_t)4 * (size_t)(B * gamma);
+    return (s + 255) & ~(size_t)255;
+}
+
+// Number of compute units of the current device (cached per device).
+int device_cu_count();
+
+// ------------------------------------------------------ internal launches
+hipError_t launch_confidence(const uint16_t *hidden, const uint16_t *w, float bias,
+                             const float *temps, int B, int gamma, int d, float *conf,
+                             float *surv, hipStream_t s);
+hipError_t launch_schedule(const float *surv, int B, int gamma, int mode, const float *cutoff,
+                           long long budget, int32_t *lengths, hipStream_t s);
+hipError_t launch_compact(const int32_t *lengths, const int32_t *tokens, int B, int gamma,
+                          int32_t *cu, int32_t *ptok, int32_t *psrc, hipStream_t s);
+hipError_t launch_gather_rows(const uint16_t *logits, const int32_t *psrc, const int32_t *cu,
+                              int B, int gamma, int V, uint16_t *out, hipStream_t s);
+hipError_t launch_accept(const uint16_t *logits, const int32_t *psrc, const int32_t *cu,
+                         const int32_t *tokens, int B, int gamma, int V, int32_t *pam,
+                         int32_t *acc, int32_t *bonus, void *ws, hipStream_t s);
+hipError_t launch_fill_zero(void *ws, size_t bytes, hipStream_t s);
+
+}  // namespace dspark

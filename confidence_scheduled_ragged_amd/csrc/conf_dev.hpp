@@ -1,0 +1,102 @@
+// conf_dev.hpp - confidence head (bf16 GEMV, fp32 accumulation, STS, sigmoid)
+// and survival product for one request, as device functions shared by the
+// stage kernel and the fused step kernel.
+//
+// [P1] "DFlash to DSpark in SGLang", section "DSpark: a sequential head and a
+// verify budget": the head is a linear projection plus a sigmoid of the
+// drafter hidden state, calibrated per block position by a temperature, and
+// the survival curve is the running product of the per-position scores.
+#pragma once
+
+#include "common.hpp"
+
+namespace dspark {
+
+// One wave per hidden row: z[i] = sum_k w[k]*h[b,i,k] + bias for the gamma rows
+// of one request. hidden_b points at row 0 of the request. kVec: d % 8 == 0
+// and both pointers 16-byte aligned, so each lane loads 8 bf16 per access.
+// w may live in LDS or global memory. The lane order of the fp32 accumulation
+// and the butterfly reduction are fixed, so results are bit-reproducible.
+template <bool kVec>
+__device__ __forceinline__ void request_logits(const uint16_t *__restrict__ hidden_b,
+                                               const uint16_t *__restrict__ w, float bias,
+                                               int gamma, int d, float *z_lds) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = threadIdx.x / kWave;
+    const int nwaves = blockDim.x / kWave;
+    for (int i = wave; i < gamma; i += nwaves) {
+        const uint16_t *h = hidden_b + (size_t)i * (size_t)d;
+        float acc = 0.0f;
+        if (kVec) {
+            const u32x4 *h4 = reinterpret_cast<const u32x4 *>(h);
+            const u32x4 *w4 = reinterpret_cast<const u32x4 *>(w);
+            const int nv = d >> 3;
+            int v = lane;
+            // four vectors per lane in flight per trip
+            for (; v + 3 * kWave < nv; v += 4 * kWave) {
+                u32x4 hv[4], wv[4];
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    hv[u] = __builtin_nontemporal_load(h4 + v + u * kWave);
+                    wv[u] = w4[v + u * kWave];
+                }
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+#pragma unroll
+                    for (int c = 0; c < 4; ++c) {
+                        acc = fmaf(bf16_lo(hv[u][c]), bf16_lo(wv[u][c]), acc);
+                        acc = fmaf(bf16_hi(hv[u][c]), bf16_hi(wv[u][c]), acc);
+                    }
+                }
+            }
+            for (; v < nv; v += kWave) {
+                u32x4 hv = __builtin_nontemporal_load(h4 + v);
+                u32x4 wv = w4[v];
+#pragma unroll
+                for (int c = 0; c < 4; ++c) {
+                    acc = fmaf(bf16_lo(hv[c]), bf16_lo(wv[c]), acc);
+                    acc = fmaf(bf16_hi(hv[c]), bf16_hi(wv[c]), acc);
+                }
+            }
+        } else {
+            for (int k = lane; k < d; k += kWave) acc = fmaf(bf16_f32(h[k]), bf16_f32(w[k]), acc);
+        }
+        acc = wave_sum_f32(acc);
+        if (lane == 0) z_lds[i] = acc + bias;
+    }
+}
+
+// Scores and survival of one request from its logits in LDS. Every thread of
+// the block calls it. p_lds and s_lds receive the scores and the survival
+// curve (both in LDS); conf_out / surv_out (global, nullable) get copies.
+// Survival is a sequential fp32 product: fl(s*p) <= s for p <= 1, so the
+// curve never increases.
+__device__ __forceinline__ void request_survival(const float *z_lds, const float *__restrict__ temps,
+                                                 int gamma, float *p_lds, float *s_lds,
+                                                 float *conf_out, float *surv_out) {
+    for (int i = threadIdx.x; i < gamma; i += blockDim.x) {
+        float p = 1.0f / (1.0f + expf(-z_lds[i] / temps[i]));
+        p_lds[i] = p;
+        if (conf_out) conf_out[i] = p;
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        float s = 1.0f;
+        for (int i = 0; i < gamma; ++i) {
+            s = s * p_lds[i];
+            s_lds[i] = s;
+        }
+    }
+    __syncthreads();
+    if (surv_out)
+        for (int i = threadIdx.x; i < gamma; i += blockDim.x) surv_out[i] = s_lds[i];
+}
+
+// Copy w (d bf16) into LDS with 16-byte accesses (kVec layout).
+__device__ __forceinline__ void stage_w(const uint16_t *__restrict__ w, int d, uint16_t *w_lds) {
+    const u32x4 *src = reinterpret_cast<const u32x4 *>(w);
+    u32x4 *dst = reinterpret_cast<u32x4 *>(w_lds);
+    for (int v = threadIdx.x; v < (d >> 3); v += blockDim.x) dst[v] = src[v];
+}
+
+}  // namespace dspark

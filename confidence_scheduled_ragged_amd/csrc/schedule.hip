@@ -1,0 +1,46 @@
+// schedule.hip - stage kernels for step 3 (verify-length cut).
+#include "sched_dev.hpp"
+
+namespace dspark {
+
+constexpr int kThreshThreads = 256;
+constexpr int kBudgetThreads = 1024;
+
+__global__ __launch_bounds__(kThreshThreads) void schedule_threshold_kernel(
+    const float *__restrict__ surv, const float *__restrict__ cutoff, int B, int gamma,
+    int32_t *__restrict__ lengths) {
+    int b = blockIdx.x * blockDim.x + threadIdx.x;
+    if (b >= B) return;
+    lengths[b] = threshold_length(surv + (size_t)b * gamma, gamma, cutoff[b]);
+}
+
+__global__ __launch_bounds__(kBudgetThreads) void schedule_budget_kernel(
+    const float *__restrict__ surv, int B, int gamma, long long budget,
+    int32_t *__restrict__ lengths) {
+    __shared__ uint32_t hist[256];
+    __shared__ uint32_t sh[2];
+    __shared__ int scan_lds[17];
+    const int N = B * gamma;
+    const int t = budget < (long long)N ? (int)budget : N;
+    if (t == 0 || t == N) {
+        for (int b = threadIdx.x; b < B; b += blockDim.x) lengths[b] = t == 0 ? 0 : gamma;
+        return;
+    }
+    BudgetCut cut = budget_select(surv, N, t, hist, sh);
+    budget_lengths(surv, B, gamma, cut, lengths, scan_lds);
+}
+
+hipError_t launch_schedule(const float *surv, int B, int gamma, int mode, const float *cutoff,
+                           long long budget, int32_t *lengths, hipStream_t s) {
+    if (mode == DSPARK_CUT_THRESHOLD) {
+        dim3 grid((B + kThreshThreads - 1) / kThreshThreads), block(kThreshThreads);
+        hipLaunchKernelGGL(schedule_threshold_kernel, grid, block, 0, s, surv, cutoff, B, gamma,
+                           lengths);
+    } else {
+        hipLaunchKernelGGL(schedule_budget_kernel, dim3(1), dim3(kBudgetThreads), 0, s, surv, B,
+                           gamma, budget, lengths);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace dspark

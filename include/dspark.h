@@ -1,0 +1,193 @@
+/*
+ * dspark.h - C ABI of the confidence-scheduled ragged verify hot path on
+ * AMD Instinct MI355X (gfx950).
+ *
+ * One speculative-decoding step of a batch of B requests, each with a drafted
+ * block of gamma tokens, runs as:
+ *   1. confidence head with per-position temperature  (dspark_confidence)
+ *   2. survival curve, the running product of scores   (dspark_confidence)
+ *   3. verify-length cut, per request or batch budget   (dspark_schedule)
+ *   4. ragged compaction into a packed verify batch     (dspark_compact)
+ *   5. greedy acceptance against the target's argmax    (dspark_accept)
+ *   6. bonus token                                      (dspark_accept)
+ * or all six in one call (dspark_step).
+ *
+ * Sources (web pages): [P1] "DFlash to DSpark in SGLang: 4.3x faster decode,
+ * and DeepSeek-V4 support" (yichizhang.dev tutorial); [P2] SGLang's DSpark
+ * announcement (24vids.com repost). Each entry point names the section of the
+ * page that defines its operation.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Every array pointer is a DEVICE pointer to memory the caller allocated and
+ *   owns. The library never allocates, frees or synchronises, keeps no state
+ *   between calls (apart from a cached per-device compute-unit count) and
+ *   does not retain any pointer after returning.
+ * - Every call enqueues its kernels on `stream` (a hipStream_t passed as
+ *   void*; NULL means the default stream) and returns without waiting. Results
+ *   are ready when the stream reaches that point.
+ * - Layouts are row-major with the last index contiguous. bf16 values are
+ *   passed as their raw 16-bit patterns (dspark_bf16).
+ * - The verify block of request b is tokens[b, 0..gamma]: column 0 is the last
+ *   committed (root) token, columns 1..gamma are the drafts. Target-logit row j
+ *   of request b (dense row b*(gamma+1)+j) scores the token that follows the
+ *   root and j drafts, so it is compared with tokens[b, j+1]; row gamma only
+ *   ever yields a bonus token.
+ * - Packed outputs have capacity B*(gamma+1), the worst case, because the
+ *   packed total is a device value. Entries at and after cu_seqlens[B] are
+ *   left untouched.
+ * - Host-side checks return a status synchronously and enqueue nothing:
+ *     DSPARK_ERR_NULL   a required pointer is NULL;
+ *     DSPARK_ERR_SHAPE  B < 1, gamma < 1, gamma > DSPARK_MAX_GAMMA, d < 1,
+ *                       V < 1, or B*(gamma+1) above DSPARK_MAX_ROWS;
+ *     DSPARK_ERR_ARG    a bad mode, a negative budget, a non-finite bias;
+ *     DSPARK_ERR_ALIGN  a pointer misaligned for its element type
+ *                       (2 bytes bf16, 4 bytes fp32/int32, 16 bytes ws);
+ *     DSPARK_ERR_WORKSPACE  ws_bytes below dspark_workspace_bytes();
+ *     DSPARK_ERR_HIP    a kernel launch failed (hipGetLastError).
+ * - Device data is never validated on the host (that would need a sync).
+ *   The kernels bound every index they use: lengths outside [0, gamma] are
+ *   clamped, a cu_seqlens total above the capacity is clamped, and a
+ *   packed_src_row entry outside the dense block gives packed_argmax = -1 for
+ *   that row. Non-finite logits or hidden values give unspecified (but
+ *   in-bounds) results; temperatures must be positive.
+ */
+#ifndef DSPARK_H
+#define DSPARK_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef uint16_t dspark_bf16;
+
+typedef enum dspark_status {
+    DSPARK_OK = 0,
+    DSPARK_ERR_NULL = 1,
+    DSPARK_ERR_SHAPE = 2,
+    DSPARK_ERR_ARG = 3,
+    DSPARK_ERR_ALIGN = 4,
+    DSPARK_ERR_WORKSPACE = 5,
+    DSPARK_ERR_HIP = 6
+} dspark_status;
+
+typedef enum dspark_cut_mode {
+    DSPARK_CUT_THRESHOLD = 0, /* per-request marginal cost cutoff[b] */
+    DSPARK_CUT_BUDGET = 1     /* batch-wide budget of `budget` drafted positions */
+} dspark_cut_mode;
+
+#define DSPARK_MAX_GAMMA 256
+#define DSPARK_MAX_ROWS (1 << 24)
+
+/*
+ * Steps 1-2 [P1, "DSpark: a sequential head and a verify budget"]: the
+ * confidence head is a linear projection plus a sigmoid of each drafted
+ * position's drafter hidden state, calibrated per position by Sequential
+ * Temperature Scaling; the block's survival curve is the running product of
+ * those scores.
+ *   conf[b,i]     = 1 / (1 + exp(-(sum_k w[k]*hidden[b,i,k] + bias) / temps[i]))
+ *   survival[b,i] = conf[b,0] * ... * conf[b,i]   (S_{i+1}; S_0 = 1 implicit)
+ * hidden [B, gamma, d] bf16; w [d] bf16; bias host fp32; temps [gamma] fp32 (> 0).
+ * conf, survival [B, gamma] fp32 outputs. Products of bf16 pairs are exact in
+ * fp32; the dot product accumulates in fp32; survival is a sequential fp32
+ * product, so it is non-increasing whenever every score is at most 1.
+ */
+dspark_status dspark_confidence(const dspark_bf16 *hidden, const dspark_bf16 *w, float bias,
+                                const float *temps, int B, int gamma, int d,
+                                float *conf, float *survival, void *stream);
+
+/*
+ * Step 3 [P1, "The confidence scheduler and verify modes" and "Zero-overhead
+ * scheduling and kernels"; P2]: choose each request's verify length L_b in
+ * [0, gamma] from its survival curve.
+ *   DSPARK_CUT_THRESHOLD: L_b = #{k in 1..gamma : survival[b,k-1] >= cutoff[b]},
+ *     the stopping point of a walk down a non-increasing curve that keeps a
+ *     draft while its survival covers the request's marginal cost. A NaN
+ *     cutoff gives 0. `budget` is ignored; cutoff is [B] fp32.
+ *   DSPARK_CUT_BUDGET: rank all B*gamma (request, position) pairs by survival
+ *     descending, ties by lower request then lower position, and keep the
+ *     first min(budget, B*gamma); L_b counts request b's kept pairs. `cutoff`
+ *     is ignored and may be NULL; budget >= 0.
+ * survival [B, gamma] fp32 (finite); lengths [B] int32 output.
+ */
+dspark_status dspark_schedule(const float *survival, int B, int gamma, int mode,
+                              const float *cutoff, long long budget, int32_t *lengths,
+                              void *stream);
+
+/*
+ * Step 4 [P1, "Ragged verify under full CUDA graphs"; "Zero-overhead
+ * scheduling and kernels" for the fused packing]: front-pack the scheduled
+ * verify rows with no padding and mark segment starts.
+ *   cu_seqlens[0] = 0, cu_seqlens[b+1] = cu_seqlens[b] + L_b + 1
+ *   packed_tokens[cu_seqlens[b] + j]  = tokens[b, j]         (j = 0..L_b)
+ *   packed_src_row[cu_seqlens[b] + j] = b*(gamma+1) + j
+ *   packed_logits[cu_seqlens[b] + j, :] = logits[b, j, :]    (optional)
+ * lengths [B] int32 (clamped to [0, gamma]); tokens [B, gamma+1] int32;
+ * cu_seqlens [B+1]; packed_tokens, packed_src_row [B*(gamma+1)] int32.
+ * logits [B, gamma+1, V] bf16 and packed_logits [B*(gamma+1), V] bf16 are
+ * either both NULL (no row gather; V is then ignored) or both non-NULL.
+ */
+dspark_status dspark_compact(const int32_t *lengths, const int32_t *tokens, int B, int gamma,
+                             int32_t *cu_seqlens, int32_t *packed_tokens,
+                             int32_t *packed_src_row, const dspark_bf16 *logits, int V,
+                             dspark_bf16 *packed_logits, void *stream);
+
+/*
+ * Steps 5-6 [P1, "Background"]: greedy verification commits the longest
+ * prefix of drafts that agree with the target's own choices, plus one bonus
+ * token from the first row that was not accepted.
+ *   packed_argmax[r] = lowest index of the largest logit of packed row r
+ *                      (-0 and +0 compare equal)
+ *   accepted[b] = largest m <= L_b with packed_argmax[cu[b]+j] == tokens[b,j+1]
+ *                 for all j < m, where L_b = cu[b+1] - cu[b] - 1
+ *   bonus[b]    = packed_argmax[cu[b] + accepted[b]]
+ * Packed row r reads dense row packed_src_row[r] of logits [B*(gamma+1), V];
+ * when packed_src_row is NULL, logits is already packed (at least cu[B] rows
+ * of V; the packed_logits output of dspark_compact has B*(gamma+1)) and row r
+ * is read directly. Only packed rows are read. cu_seqlens [B+1] and
+ * tokens [B, gamma+1] int32 inputs; packed_argmax [B*(gamma+1)], accepted
+ * and bonus [B] int32 outputs. ws: scratch of at least
+ * dspark_workspace_bytes(B, gamma, V) bytes, 16-byte aligned.
+ */
+dspark_status dspark_accept(const dspark_bf16 *logits, const int32_t *packed_src_row,
+                            const int32_t *cu_seqlens, const int32_t *tokens, int B, int gamma,
+                            int V, int32_t *packed_argmax, int32_t *accepted, int32_t *bonus,
+                            void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * Steps 1-6 fused, the production "compact" verify mode of [P1, "The
+ * confidence scheduler and verify modes"]: the result equals dspark_confidence
+ * -> dspark_schedule -> dspark_compact -> dspark_accept on the same inputs,
+ * with the dense logits [B, gamma+1, V] read only at packed rows.
+ * conf and survival may be NULL when the caller does not want them. ws must be
+ * zero-filled before its first use with this entry point (dspark_workspace_init
+ * does it on a stream); every call leaves it zero-filled again on completion.
+ * Calls that share a workspace must not overlap in time.
+ */
+dspark_status dspark_step(const dspark_bf16 *hidden, const dspark_bf16 *w, float bias,
+                          const float *temps, const int32_t *tokens, const dspark_bf16 *logits,
+                          int B, int gamma, int d, int V, int mode, const float *cutoff,
+                          long long budget, float *conf, float *survival, int32_t *lengths,
+                          int32_t *cu_seqlens, int32_t *packed_tokens, int32_t *packed_src_row,
+                          int32_t *packed_argmax, int32_t *accepted, int32_t *bonus,
+                          void *ws, size_t ws_bytes, void *stream);
+
+/* Scratch bytes needed by dspark_accept and dspark_step for these sizes
+ * (independent of d); 0 for invalid sizes. */
+size_t dspark_workspace_bytes(int B, int gamma, int V);
+
+/* Zero-fill a workspace on `stream` with a kernel (no memset node, so it can
+ * be captured in a graph). */
+dspark_status dspark_workspace_init(void *ws, size_t ws_bytes, void *stream);
+
+/* Static, NUL-terminated description of a status code. */
+const char *dspark_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DSPARK_H */
