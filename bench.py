@@ -32,6 +32,40 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_dspark_step_mixed_threshold.txt")
+CSRC = os.path.join(ROOT, "confidence_scheduled_ragged_amd", "csrc")
+
+
+def kernel_source_digest() -> str:
+    """sha256 over the HIP sources, to tell whether recorded counters still
+    describe the kernels being timed."""
+    import hashlib
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(CSRC)):
+        if name.endswith((".hip", ".hpp")):
+            with open(os.path.join(CSRC, name), "rb") as f:
+                h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()
+
+
+def recorded_traffic():
+    """HBM bytes per step from the committed rocprofv3 counter summary
+    (FETCH_SIZE + WRITE_SIZE scaled by the copy-kernel factor), or None when
+    there is none or the kernels changed since it was taken."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    kv = {}
+    with open(TRAFFIC_FILE) as f:
+        for line in f:
+            if "=" in line and not line.startswith("#"):
+                k, v = line.split("=", 1)
+                kv[k.strip()] = v.strip()
+    if kv.get("source_sha256") != kernel_source_digest():
+        return None
+    try:
+        return float(kv["hbm_bytes_per_step"])
+    except (KeyError, ValueError):
+        return None
 
 
 def log(msg):
@@ -63,8 +97,15 @@ def run_arm(cfg, slots, outs, ws, steps, warmup, dspark, torch):
         dspark.dspark_step(s.hidden, s.w, s.bias, s.temps, s.tokens, s.logits, cfg.mode,
                            cutoff=s.cutoff, budget=cfg.budget, out=outs[i % R], ws=ws)
 
-    for i in range(warmup):
+    # warm up by count and by time: after an idle period the clocks need a few
+    # milliseconds of load before they settle
+    t_w = time.perf_counter()
+    i = 0
+    while i < warmup or time.perf_counter() - t_w < 0.2:
         launch(i)
+        i += 1
+        if i % 64 == 0:
+            torch.cuda.synchronize()
     torch.cuda.synchronize()
     totals = [int(o["cu_seqlens"][-1].item()) for o in outs]
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
@@ -162,6 +203,9 @@ def main():
     ap.add_argument("--rotation", type=int, default=8)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra-arms", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="also run a 1 GiB device-to-device copy (a plain copy kernel of known "
+                         "size) so counter runs can scale FETCH_SIZE / WRITE_SIZE")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU: the verify hot path runs on a single MI355X here "
@@ -194,6 +238,20 @@ def main():
         f"{s_t['achieved_gbs']:.0f} GB/s ({100 * s_t['frac_of_hbm_peak']:.1f} % of peak)")
 
     extra = {}
+    if not args.no_extra_arms:
+        # budget arm on the same resident batches (the two arms share their seeds)
+        r_b = run_arm(cfg_b, slots, outs, ws, args.steps, args.warmup, dspark, torch)
+        extra["mixed_budget_T742"] = arm_summary(cfg_b, r_b, args.steps, cfg_b.B)
+        log(f"budget arm: {extra['mixed_budget_T742']['rows_per_s']:.3e} rows/s")
+        cfg4 = CONFIGS["budget"]
+        p4 = make_params(cfg4)
+        slots4 = [make_step(cfg4, i, device=dev, params=p4) for i in range(args.rotation)]
+        outs4 = [dspark.alloc_step_outputs(cfg4.B, cfg4.gamma, dev) for _ in slots4]
+        ws4 = dspark.workspace(cfg4.B, cfg4.gamma, cfg4.V, dev)
+        r_4 = run_arm(cfg4, slots4, outs4, ws4, args.steps, args.warmup, dspark, torch)
+        extra["budget_d7168_V129280_T768"] = arm_summary(cfg4, r_4, args.steps, cfg4.B)
+        log(f"budget d=7168 arm: {extra['budget_d7168_V129280_T768']['rows_per_s']:.3e} rows/s")
+
     cpu = None
     parity = None
     if not args.no_cpu_baseline:
@@ -210,21 +268,15 @@ def main():
         cpu.pop("seconds", None)
         log(f"oracle: {cpu['value']:.1f} rows/s on 1 core; parity on sampled batches: {parity}")
 
-    if not args.no_extra_arms:
-        # budget arm on the same resident batches (the two arms share their seeds)
-        r_b = run_arm(cfg_b, slots, outs, ws, args.steps, args.warmup, dspark, torch)
-        extra["mixed_budget_T742"] = arm_summary(cfg_b, r_b, args.steps, cfg_b.B)
-        log(f"budget arm: {extra['mixed_budget_T742']['rows_per_s']:.3e} rows/s")
-        del slots, outs
-        torch.cuda.empty_cache()
-        cfg4 = CONFIGS["budget"]
-        p4 = make_params(cfg4)
-        slots4 = [make_step(cfg4, i, device=dev, params=p4) for i in range(args.rotation)]
-        outs4 = [dspark.alloc_step_outputs(cfg4.B, cfg4.gamma, dev) for _ in slots4]
-        ws4 = dspark.workspace(cfg4.B, cfg4.gamma, cfg4.V, dev)
-        r_4 = run_arm(cfg4, slots4, outs4, ws4, args.steps, args.warmup, dspark, torch)
-        extra["budget_d7168_V129280_T768"] = arm_summary(cfg4, r_4, args.steps, cfg4.B)
-        log(f"budget d=7168 arm: {extra['budget_d7168_V129280_T768']['rows_per_s']:.3e} rows/s")
+    if args.calibrate_copy:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log("copy calibration: 3 x 1 GiB device-to-device copies done")
+        del src, dst
 
     mean_bytes = r_t["bytes"] / args.steps
     line = {
@@ -247,11 +299,12 @@ def main():
                    "mean_packed_rows": s_t["mean_packed_rows"]},
         "request_steps_per_s": s_t["request_steps_per_s"],
         "achieved_gbs": s_t["achieved_gbs"],
-        "roofline": {"bound": "hbm", "kernel": "dspark_step",
+        "roofline": {"bound": "hbm",
+                     "kernel": "dspark_step = step_front_kernel + step_back_kernel (one stream)",
                      "achieved": mean_bytes / (r_t["mean_step_ms"] / 1e3) / 1e9,
                      "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": mean_bytes / (r_t["mean_step_ms"] / 1e3) / 1e9 / HBM_PEAK_GBS,
-                     "traffic": None,
+                     "traffic": recorded_traffic(),
                      "algorithmic_bytes_per_launch": mean_bytes,
                      "mean_launch_us": r_t["mean_step_ms"] * 1e3},
         "cpu_baseline": cpu,

@@ -103,14 +103,27 @@ __device__ __forceinline__ void wave_argmax_share(const uint16_t *__restrict__ l
     }
 }
 
+// Keys written and read inside one kernel by different workgroups (possibly on
+// different XCDs, each with its own L2) use device-coherent accesses: the
+// store writes through to the device coherence point and the load bypasses
+// any stale L2 copy. Neither needs an L2-wide write-back or invalidate.
+__device__ __forceinline__ void store_key_coherent(uint64_t *p, uint64_t v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint64_t load_key_coherent(const uint64_t *p) {
+    return __hip_atomic_load(const_cast<uint64_t *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 // Argmax of packed row r from the keys of the waves whose shares touch it.
+// kCoherent: the keys were written by this same kernel.
+template <bool kCoherent = false>
 __device__ __forceinline__ int32_t row_argmax(const uint64_t *__restrict__ keys, int64_t r,
                                               int64_t Vv, int64_t Q) {
     const int64_t w_lo = (r * Vv) / Q;
     const int64_t w_hi = ((r + 1) * Vv - 1) / Q;
     uint64_t k = 0;
     for (int64_t w = w_lo; w <= w_hi; ++w) {
-        const uint64_t x = keys[w + r];
+        const uint64_t x = kCoherent ? load_key_coherent(keys + w + r) : keys[w + r];
         k = x > k ? x : k;
     }
     return key_index(k);
@@ -119,6 +132,7 @@ __device__ __forceinline__ int32_t row_argmax(const uint64_t *__restrict__ keys,
 // Acceptance and bonus of request b by one wave: lane j handles packed row
 // cu[b] + j (chunks of 64 rows). The first row j where the target disagrees
 // with draft j+1, or j = L_b, is the accepted count; its argmax is the bonus.
+template <bool kCoherent = false>
 __device__ __forceinline__ void wave_accept_request(const uint64_t *__restrict__ keys,
                                                     const int32_t *__restrict__ cu,
                                                     const int32_t *__restrict__ tokens, int b,
@@ -141,21 +155,26 @@ __device__ __forceinline__ void wave_accept_request(const uint64_t *__restrict__
     const int L = n - 1 < gamma ? n - 1 : gamma;
     const int32_t *tok = tokens + (size_t)b * (gamma + 1);
     int a = -1;
+    int32_t bon = -1;
     for (int j0 = 0; j0 < n; j0 += kWave) {
         const int j = j0 + lane;
         int32_t am = -1;
         bool stop = false;
         if (j < n) {
-            am = row_argmax(keys, start + j, Vv, Q);
+            am = row_argmax<kCoherent>(keys, start + j, Vv, Q);
             pam[start + j] = am;
             stop = (j >= L) || (am != tok[j + 1]);
         }
         const uint64_t mask = __ballot(stop);
-        if (a < 0 && mask != 0ull) a = j0 + __ffsll((unsigned long long)mask) - 1;
+        if (a < 0 && mask != 0ull) {
+            const int first = __ffsll((unsigned long long)mask) - 1;
+            a = j0 + first;
+            bon = __shfl(am, first, kWave);  // the bonus is that row's argmax
+        }
     }
     if (lane == 0) {
         acc[b] = a;
-        bonus[b] = row_argmax(keys, start + a, Vv, Q);
+        bonus[b] = bon;
     }
 }
 

@@ -180,10 +180,14 @@ DSPARK_API dspark_status dspark_step(const dspark_bf16 *hidden, const dspark_bf1
     if (ws_bytes < ws_total_bytes(B, gamma)) return DSPARK_ERR_WORKSPACE;
     hipStream_t s = as_stream(stream);
     char *wsb = static_cast<char *>(ws);
-    float *surv = survival ? survival
-                           : reinterpret_cast<float *>(wsb + ws_surv_offset((int64_t)B * (gamma + 1)));
+    float *surv = survival ? survival : reinterpret_cast<float *>(wsb + ws_surv_offset(B, gamma));
     float *cf = conf ? conf : reinterpret_cast<float *>(wsb + ws_conf_offset(B, gamma));
-    hipError_t e = launch_confidence(hidden, w, bias, temps, B, gamma, d, cf, surv, s);
+    hipError_t e = launch_fused_step(hidden, w, bias, temps, tokens, logits, B, gamma, d, V, mode,
+                                     cutoff, budget, cf, surv, lengths, cu_seqlens, packed_tokens,
+                                     packed_src_row, packed_argmax, accepted, bonus, ws, s);
+    if (e != hipErrorNotSupported) return launched(e);
+    // sizes outside the fused kernels' limits: the same step through the stage kernels
+    e = launch_confidence(hidden, w, bias, temps, B, gamma, d, cf, surv, s);
     if (e == hipSuccess) e = launch_schedule(surv, B, gamma, mode, cutoff, budget, lengths, s);
     if (e == hipSuccess)
         e = launch_compact(lengths, tokens, B, gamma, cu_seqlens, packed_tokens, packed_src_row, s);

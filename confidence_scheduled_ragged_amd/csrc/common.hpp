@@ -76,19 +76,36 @@ __device__ __forceinline__ int64_t partition_q(int64_t E, int64_t W) {
 }
 
 // ------------------------------------------------------------ workspace map
-// [0, 256)                          control words (fused step; self-cleaning)
-// [256, 256 + 8*(kMaxWaves + cap))   argmax segment keys (cap = B*(gamma+1))
-// then float [B*gamma]               survival scratch (when the caller passes none)
-// then float [B*gamma]               score scratch (when the caller passes none)
+// [0, 256)                        control words of the fused step: the step
+//                                 epoch (offset 0) and the schedule flag
+//                                 (offset 128), each on its own cache line
+// keys:  uint64 [kMaxWaves + cap] argmax segment keys (cap = B*(gamma+1));
+//                                 the fused step keeps its draft rows here
+// keys0: uint64 [kMaxWaves + B]   segment keys of the root rows (fused step)
+// cnt:   uint64 [B]               per-request completion counters (fused step)
+// len:   int32 [B] (+pad)         published verify lengths (fused step, budget)
+// surv:  float [B*gamma]          survival scratch (when the caller passes none)
+// conf:  float [B*gamma]          score scratch (when the caller passes none)
 constexpr int64_t kMaxWaves = 16384;
 constexpr size_t kCtrlBytes = 256;
+constexpr size_t kEpochOffset = 0;
+constexpr size_t kFlagOffset = 128;
 
 inline size_t ws_keys_offset() { return kCtrlBytes; }
-inline size_t ws_surv_offset(int64_t cap) {
-    return kCtrlBytes + (size_t)8 * (size_t)(kMaxWaves + cap);
+inline size_t ws_keys0_offset(int64_t B, int64_t gamma) {
+    return ws_keys_offset() + (size_t)8 * (size_t)(kMaxWaves + B * (gamma + 1));
+}
+inline size_t ws_cnt_offset(int64_t B, int64_t gamma) {
+    return ws_keys0_offset(B, gamma) + (size_t)8 * (size_t)(kMaxWaves + B);
+}
+inline size_t ws_len_offset(int64_t B, int64_t gamma) {
+    return ws_cnt_offset(B, gamma) + (size_t)8 * (size_t)B;
+}
+inline size_t ws_surv_offset(int64_t B, int64_t gamma) {
+    return ws_len_offset(B, gamma) + (size_t)8 * (size_t)((B + 1) / 2);
 }
 inline size_t ws_conf_offset(int64_t B, int64_t gamma) {
-    return ws_surv_offset(B * (gamma + 1)) + (size_t)4 * (size_t)(B * gamma);
+    return ws_surv_offset(B, gamma) + (size_t)4 * (size_t)(B * gamma);
 }
 inline size_t ws_total_bytes(int64_t B, int64_t gamma) {
     size_t s = ws_conf_offset(B, gamma) + (size_t)4 * (size_t)(B * gamma);
@@ -112,5 +129,15 @@ hipError_t launch_accept(const uint16_t *logits, const int32_t *psrc, const int3
                          const int32_t *tokens, int B, int gamma, int V, int32_t *pam,
                          int32_t *acc, int32_t *bonus, void *ws, hipStream_t s);
 hipError_t launch_fill_zero(void *ws, size_t bytes, hipStream_t s);
+
+// The fused step in two launches. Returns hipErrorNotSupported (enqueuing
+// nothing) when the sizes are outside what it handles; the caller then runs
+// the stage kernels instead.
+hipError_t launch_fused_step(const uint16_t *hidden, const uint16_t *w, float bias,
+                             const float *temps, const int32_t *tokens, const uint16_t *logits,
+                             int B, int gamma, int d, int V, int mode, const float *cutoff,
+                             long long budget, float *conf, float *surv, int32_t *lengths,
+                             int32_t *cu, int32_t *ptok, int32_t *psrc, int32_t *pam,
+                             int32_t *acc, int32_t *bonus, void *ws, hipStream_t s);
 
 }  // namespace dspark

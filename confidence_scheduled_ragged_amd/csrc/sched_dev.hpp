@@ -119,6 +119,81 @@ __device__ __forceinline__ BudgetCut budget_select(const float *__restrict__ sur
     return r;
 }
 
+// Budget select for the fused step: the same radix select as budget_select,
+// but each thread holds a contiguous run of up to kPer flat positions in
+// registers (N <= kPer * blockDim.x). Neighbouring positions of one request
+// have non-increasing survival, so their digits often repeat; equal digits of
+// consecutive positions are counted once per run, which keeps the LDS
+// histogram atomics off the few crowded bins.
+template <int kPer>
+__device__ __forceinline__ BudgetCut budget_select_runs(const float *__restrict__ surv, int N, int t,
+                                                        uint32_t *hist /*256*/, uint32_t *sh /*2*/) {
+    const int tid = threadIdx.x;
+    const int bd = blockDim.x;
+    const int lane = tid & (kWave - 1);
+    const int per = (N + bd - 1) / bd;
+    const int f0 = tid * per;
+    uint32_t v[kPer];
+    int nv = 0;
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+        const int f = f0 + j;
+        const bool ok = j < per && f < N;
+        v[j] = ok ? ordered_f32(surv[f]) : 0u;
+        nv += ok ? 1 : 0;
+    }
+    uint32_t prefix = 0, mask = 0;
+    uint32_t remaining = (uint32_t)t;
+    for (int shift = 24; shift >= 0; shift -= 8) {
+        for (int i = tid; i < 256; i += bd) hist[i] = 0;
+        __syncthreads();
+        uint32_t cur = 0xFFFFFFFFu, run = 0;
+#pragma unroll
+        for (int j = 0; j < kPer; ++j) {
+            if (j < nv && (v[j] & mask) == prefix) {
+                const uint32_t dg = (v[j] >> shift) & 255u;
+                if (dg == cur) {
+                    ++run;
+                } else {
+                    if (run) atomicAdd(&hist[cur], run);
+                    cur = dg;
+                    run = 1;
+                }
+            }
+        }
+        if (run) atomicAdd(&hist[cur], run);
+        __syncthreads();
+        if (tid < kWave) {
+            uint32_t c[4];
+            uint32_t tot = 0;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                c[q] = hist[255 - 4 * lane - q];
+                tot += c[q];
+            }
+            const int inc = wave_incl_scan((int)tot, lane);
+            uint32_t cum = (uint32_t)inc - tot;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                if (cum < remaining && remaining <= cum + c[q]) {
+                    sh[0] = prefix | ((uint32_t)(255 - 4 * lane - q) << shift);
+                    sh[1] = remaining - cum;
+                }
+                cum += c[q];
+            }
+        }
+        __syncthreads();
+        prefix = sh[0];
+        remaining = sh[1];
+        mask |= 0xFFu << shift;
+        __syncthreads();
+    }
+    BudgetCut r;
+    r.tau = prefix;
+    r.need = (int)remaining;
+    return r;
+}
+
 // Lengths from a budget cut for requests [0, B): L_b = #{v > tau} + the
 // request's share of the `need` tied picks, handed out in request order.
 // Every thread calls it. lds needs 17 ints.

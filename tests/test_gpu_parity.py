@@ -276,7 +276,8 @@ def test_step_mixed_workload(name):
 
 
 @pytest.mark.parametrize("case", ["gamma1", "all_zero", "all_full", "budget0", "budget_all",
-                                  "nan_cut", "odd_vocab", "tiny_vocab", "big_gamma"])
+                                  "nan_cut", "odd_vocab", "tiny_vocab", "big_gamma",
+                                  "stage_path_budget", "stage_path_wide"])
 def test_step_edge_cases(case):
     base = CONFIGS["tiny"]
     cfg = {
@@ -289,6 +290,10 @@ def test_step_edge_cases(case):
         "odd_vocab": base.scaled(V=1001, d=250),
         "tiny_vocab": base.scaled(V=3, B=7),
         "big_gamma": base.scaled(gamma=64, B=3, V=4096),
+        # beyond the fused kernels' limits (B*gamma > 8192 in budget mode, B > 4096):
+        # dspark_step runs the stage kernels
+        "stage_path_budget": CONFIGS["mixed_budget"].scaled(B=600, d=256, V=512),
+        "stage_path_wide": base.scaled(B=4200, gamma=2, d=64, V=64),
     }[case]
     _run_workload(cfg, range(3), case)
 
