@@ -300,7 +300,7 @@ def main():
         "request_steps_per_s": s_t["request_steps_per_s"],
         "achieved_gbs": s_t["achieved_gbs"],
         "roofline": {"bound": "hbm",
-                     "kernel": "dspark_step = step_front_kernel + step_back_kernel (one stream)",
+                     "kernel": "dspark_step = step_front_kernel + step_stream_kernel + step_finish_kernel (one stream; budget mode adds schedule_budget_kernel)",
                      "achieved": mean_bytes / (r_t["mean_step_ms"] / 1e3) / 1e9,
                      "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": mean_bytes / (r_t["mean_step_ms"] / 1e3) / 1e9 / HBM_PEAK_GBS,

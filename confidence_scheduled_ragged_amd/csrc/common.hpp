@@ -76,39 +76,29 @@ __device__ __forceinline__ int64_t partition_q(int64_t E, int64_t W) {
 }
 
 // ------------------------------------------------------------ workspace map
-// [0, 256)                        control words of the fused step: the step
-//                                 epoch (offset 0) and the schedule flag
-//                                 (offset 128), each on its own cache line
-// keys:  uint64 [kMaxWaves + cap] argmax segment keys (cap = B*(gamma+1));
-//                                 the fused step keeps its draft rows here
-// keys0: uint64 [kMaxWaves + B]   segment keys of the root rows (fused step)
-// cnt:   uint64 [B]               per-request completion counters (fused step)
-// len:   int32 [B] (+pad)         published verify lengths (fused step, budget)
-// surv:  float [B*gamma]          survival scratch (when the caller passes none)
-// conf:  float [B*gamma]          score scratch (when the caller passes none)
-constexpr int64_t kMaxWaves = 16384;
-constexpr size_t kCtrlBytes = 256;
-constexpr size_t kEpochOffset = 0;
-constexpr size_t kFlagOffset = 128;
+// keys:  uint64 [key_slots(B,gamma,V)] argmax segment keys
+// surv:  float [B*gamma]         survival scratch (when the caller passes none)
+// conf:  float [B*gamma]         score scratch (when the caller passes none)
+constexpr int64_t kMaxWaves = 16384;   // resident waves of the static argmax grid
+constexpr int64_t kSubSlots = 1024;    // 16-byte slots per fused-step sub-chunk (16 KiB)
 
-inline size_t ws_keys_offset() { return kCtrlBytes; }
-inline size_t ws_keys0_offset(int64_t B, int64_t gamma) {
-    return ws_keys_offset() + (size_t)8 * (size_t)(kMaxWaves + B * (gamma + 1));
+// Key slots: the stage argmax keeps one key per (wave, row) segment (index
+// w + r, w < kMaxWaves); the fused step one per (sub-chunk, row) segment
+// (index s + r). Sized for the scalar layout (one bf16 per slot), the larger.
+inline int64_t key_slots(int64_t B, int64_t gamma, int64_t V) {
+    const int64_t cap = B * (gamma + 1);
+    const int64_t sub = (cap * V + kSubSlots - 1) / kSubSlots;
+    return (sub > kMaxWaves ? sub : kMaxWaves) + cap;
 }
-inline size_t ws_cnt_offset(int64_t B, int64_t gamma) {
-    return ws_keys0_offset(B, gamma) + (size_t)8 * (size_t)(kMaxWaves + B);
+inline size_t ws_keys_offset() { return 0; }
+inline size_t ws_surv_offset(int64_t B, int64_t gamma, int64_t V) {
+    return ws_keys_offset() + (size_t)8 * (size_t)key_slots(B, gamma, V);
 }
-inline size_t ws_len_offset(int64_t B, int64_t gamma) {
-    return ws_cnt_offset(B, gamma) + (size_t)8 * (size_t)B;
+inline size_t ws_conf_offset(int64_t B, int64_t gamma, int64_t V) {
+    return ws_surv_offset(B, gamma, V) + (size_t)4 * (size_t)(B * gamma);
 }
-inline size_t ws_surv_offset(int64_t B, int64_t gamma) {
-    return ws_len_offset(B, gamma) + (size_t)8 * (size_t)((B + 1) / 2);
-}
-inline size_t ws_conf_offset(int64_t B, int64_t gamma) {
-    return ws_surv_offset(B, gamma) + (size_t)4 * (size_t)(B * gamma);
-}
-inline size_t ws_total_bytes(int64_t B, int64_t gamma) {
-    size_t s = ws_conf_offset(B, gamma) + (size_t)4 * (size_t)(B * gamma);
+inline size_t ws_total_bytes(int64_t B, int64_t gamma, int64_t V) {
+    size_t s = ws_conf_offset(B, gamma, V) + (size_t)4 * (size_t)(B * gamma);
     return (s + 255) & ~(size_t)255;
 }
 

@@ -1,23 +1,24 @@
-// fused.hip - the whole verify step in two launches, with no grid-wide wait.
+// fused.hip - the whole verify step as a short chain of launches on one stream.
 //
-// Launch 1 (front, one workgroup per request): the confidence GEMV of the
-// request's gamma hidden rows (one wave per row), the STS sigmoid, the
-// sequential survival product and, in threshold mode, the verify length. It
-// also zeroes the request's completion counter for launch 2.
+//   front   one workgroup per request: the confidence GEMV of the request's gamma
+//           hidden rows (one wave per row), the STS sigmoid, the sequential
+//           survival product and, in threshold mode, the verify length.
+//   select  (budget mode only) one workgroup: the batch-wide top-T pick over all
+//           survival values and each request's verify length.
+//   stream  a persistent grid: every workgroup scans the verify lengths into
+//           cu_seqlens in LDS and writes the schedule outputs of its own
+//           requests; then the packed logit rows of all requests, laid end to
+//           end and cut into 16 KiB sub-chunks, are streamed: each wave leaves
+//           one argmax key per row segment of each sub-chunk it reads. The
+//           sub-chunks are dealt out cyclically over all resident waves.
+//   finish  one wave per request: each packed row's argmax from its keys, the
+//           longest agreeing prefix and the bonus token.
 //
-// Launch 2 (back, a persistent grid sized to be resident at once):
-//   * every workgroup derives the whole schedule on its own from launch 1's
-//     results (in budget mode a radix select over the batch's survival values)
-//     and scans the verify lengths into cu_seqlens in LDS; workgroup k writes
-//     the schedule outputs of requests k, k+G, ... ;
-//   * the packed rows of all requests, laid end to end, are cut into one
-//     contiguous slice per wave; each wave streams its slice and leaves one
-//     argmax key per row segment;
-//   * when all waves of a workgroup are done, the workgroup adds the number of
-//     slots it finished to each request it touched; the workgroup whose
-//     addition completes a request computes that request's acceptance and
-//     bonus token. No wave ever waits for another workgroup, so the kernel
-//     cannot deadlock and needs no co-residency guarantee.
+// Small cyclic sub-chunks spread the rows of every request over the whole
+// chip. Dynamic hand-out through per-XCD atomic work queues was measured
+// slower: one queue serves about one ticket per 11 ns, and even a queue that
+// serves only the last fifth of the sub-chunks cost 2-6 us per step. Grid-wide
+// waits were measured at 16-76 us each and are not used.
 //
 // [P1] "DFlash to DSpark in SGLang", sections "DSpark: a sequential head and a
 // verify budget" (head, survival, cut), "Ragged verify under full CUDA graphs"
@@ -34,12 +35,10 @@ namespace dspark {
 
 constexpr int kFrontThreads = 1024;
 constexpr int kFrontMaxLdsW = 16384;
-constexpr int kBackThreads = 512;
-constexpr int kBackWaves = kBackThreads / kWave;
-constexpr int kBackUnroll = 8;
-constexpr int kSelPerThread = 16;                        // budget values per thread
-constexpr int kMaxFusedB = 4096;                         // LDS: 8*B + 4 bytes
-constexpr int kMaxFusedBudgetN = kSelPerThread * kBackThreads;
+constexpr int kStreamThreads = 512;
+constexpr int kStreamUnroll = 8;
+constexpr int kFinishThreads = 256;
+constexpr int kMaxFusedB = 4096;  // LDS of the stream kernel: 8*B + 4 bytes
 
 // ------------------------------------------------------------------ front
 
@@ -50,7 +49,6 @@ struct FrontParams {
     int gamma, d, mode;
     float *conf, *surv;
     int32_t *lengths;
-    unsigned long long *cnt;
 };
 
 template <bool kVecH, bool kLdsW>
@@ -68,23 +66,19 @@ __global__ __launch_bounds__(kFrontThreads) void step_front_kernel(FrontParams p
     __syncthreads();
     request_survival(z_s, p.temps, p.gamma, p_s, s_s, p.conf + (size_t)b * p.gamma,
                      p.surv + (size_t)b * p.gamma);
-    if (threadIdx.x == 0) {
-        if (p.mode == DSPARK_CUT_THRESHOLD)
-            p.lengths[b] = threshold_length(s_s, p.gamma, p.cutoff[b]);
-        p.cnt[b] = 0ull;
-    }
+    if (threadIdx.x == 0 && p.mode == DSPARK_CUT_THRESHOLD)
+        p.lengths[b] = threshold_length(s_s, p.gamma, p.cutoff[b]);
 }
 
-// ------------------------------------------------------------------- back
+// ----------------------------------------------------------------- stream
 
-struct BackParams {
+struct StreamParams {
     const uint16_t *logits;
     const int32_t *tokens;
-    const float *surv;
-    int B, gamma, V, mode, t_eff, W;
-    int32_t *lengths, *cu, *ptok, *psrc, *pam, *acc, *bonus;
+    const int32_t *lengths;
+    int B, gamma, V;
+    int32_t *cu, *ptok, *psrc;
     uint64_t *keys;
-    unsigned long long *cnt;
 };
 
 // Largest b in [0, B] with cu[b] <= r (cu non-decreasing, cu[0] = 0 <= r):
@@ -99,39 +93,21 @@ __device__ __forceinline__ int row_owner(const int *cu, int B, int64_t r) {
 }
 
 template <bool kVec>
-__global__ __launch_bounds__(kBackThreads) void step_back_kernel(BackParams p) {
+__global__ __launch_bounds__(kStreamThreads) void step_stream_kernel(StreamParams p) {
     extern __shared__ int smem[];
     int *len_s = smem;          // [B]
     int *cu_s = smem + p.B;     // [B + 1]
-    __shared__ uint32_t hist[256];
-    __shared__ uint32_t sh[2];
     __shared__ int scan_lds[17];
-    __shared__ int done_s[kBackThreads];
-    __shared__ int ndone_s;
     const int B = p.B, g = p.gamma, g1 = p.gamma + 1;
     const int tid = threadIdx.x, bd = blockDim.x;
     const int lane = tid & (kWave - 1);
-    const int wave = tid / kWave;
-    const int nw = bd / kWave;
 
-    // 1. verify lengths, derived independently by every workgroup
-    if (p.mode == DSPARK_CUT_THRESHOLD) {
-        for (int b = tid; b < B; b += bd) {
-            const int L = p.lengths[b];
-            len_s[b] = L < 0 ? 0 : (L > g ? g : L);
-        }
-    } else {
-        const int N = B * g;
-        if (p.t_eff == 0 || p.t_eff == N) {
-            for (int b = tid; b < B; b += bd) len_s[b] = p.t_eff == 0 ? 0 : g;
-        } else {
-            const BudgetCut cut = budget_select_runs<kSelPerThread>(p.surv, N, p.t_eff, hist, sh);
-            budget_lengths(p.surv, B, g, cut, len_s, scan_lds);
-        }
+    // schedule: lengths (clamped), cu_seqlens in LDS, this workgroup's outputs
+    for (int b = tid; b < B; b += bd) {
+        const int L = p.lengths[b];
+        len_s[b] = L < 0 ? 0 : (L > g ? g : L);
     }
     __syncthreads();
-
-    // 2. cu_seqlens in LDS
     int carry = 0;
     for (int base = 0; base < B; base += bd) {
         const int b = base + tid;
@@ -143,12 +119,9 @@ __global__ __launch_bounds__(kBackThreads) void step_back_kernel(BackParams p) {
     }
     if (tid == 0) cu_s[B] = carry;
     __syncthreads();
-    // schedule outputs: workgroup k writes those of requests k, k+G, ... (a
-    // few entries each), so no workgroup starts its slice late
     for (int b = blockIdx.x; b < B; b += gridDim.x) {
         if (tid == 0) {
             p.cu[b + 1] = cu_s[b + 1];
-            if (p.mode != DSPARK_CUT_THRESHOLD) p.lengths[b] = len_s[b];
             if (b == 0) p.cu[0] = 0;
         }
         for (int j = tid; j <= len_s[b]; j += bd) {
@@ -157,74 +130,54 @@ __global__ __launch_bounds__(kBackThreads) void step_back_kernel(BackParams p) {
         }
     }
 
+    // sub-chunks of the packed rows, dealt out cyclically: wave w of W streams
+    // sub-chunks w, w + W, w + 2W, ... (no atomics, no waits)
     const int64_t Vv = kVec ? (p.V >> 3) : p.V;
-    const int total = cu_s[B];
-    const int64_t E = (int64_t)total * Vv;  // slots of all packed rows
-    const int64_t Q = partition_q(E, p.W);
-    const int64_t w = (int64_t)blockIdx.x * nw + wave;
-
-    // 3. this wave's slice of the packed rows
-    int64_t e = w * Q;
-    const int64_t e_end = e + Q < E ? e + Q : E;
-    int64_t r = e / Vv;
-    while (e < e_end) {
-        const int64_t row_end = (r + 1) * Vv;
-        const int64_t seg_end = e_end < row_end ? e_end : row_end;
-        const int b = row_owner(cu_s, B, r);
-        const int64_t src = (int64_t)b * g1 + (r - cu_s[b]);
-        float best = -INFINITY;
-        int bidx = -1;
-        lane_row_segment<kVec, kBackUnroll>(p.logits + (size_t)src * (size_t)p.V, e - r * Vv,
-                                            seg_end - r * Vv, lane, best, bidx);
-        uint64_t key = bidx >= 0 ? argmax_key(best, (uint32_t)bidx) : 0ull;
-        key = wave_max_u64(key);
-        if (lane == 0) store_key_coherent(p.keys + w + r, key);
-        e = seg_end;
-        ++r;
-    }
-    // every key store of this wave is performed before the workgroup counts
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-
-    // 4. count this workgroup's finished slots per touched request; the
-    //    workgroup that completes a request finishes it
-    const int64_t g0 = (int64_t)blockIdx.x * nw * Q;
-    int64_t g_end = g0 + (int64_t)nw * Q;
-    g_end = g_end < E ? g_end : E;
-    if (g0 >= g_end) return;  // no barrier follows
-    const int b_first = row_owner(cu_s, B, g0 / Vv);
-    const int b_last = row_owner(cu_s, B, (g_end - 1) / Vv);
-    for (int base = b_first; base <= b_last; base += bd) {
-        if (tid == 0) ndone_s = 0;
-        __syncthreads();
-        const int b = base + tid;
-        if (b <= b_last) {
-            const int64_t lo0 = (int64_t)cu_s[b] * Vv;
-            const int64_t hi0 = (int64_t)cu_s[b + 1] * Vv;
-            const int64_t lo = lo0 > g0 ? lo0 : g0;
-            const int64_t hi = hi0 < g_end ? hi0 : g_end;
-            if (hi > lo) {
-                const unsigned long long mine = (unsigned long long)(hi - lo);
-                const unsigned long long old = __hip_atomic_fetch_add(
-                    p.cnt + b, mine, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                if (old + mine == (unsigned long long)(hi0 - lo0)) done_s[atomicAdd(&ndone_s, 1)] = b;
-            }
+    const int64_t E = (int64_t)cu_s[B] * Vv;
+    const int64_t NS = (E + kSubSlots - 1) / kSubSlots;
+    const int64_t W = (int64_t)gridDim.x * (bd / kWave);
+    for (int64_t cur = (int64_t)blockIdx.x * (bd / kWave) + tid / kWave; cur < NS; cur += W) {
+        // stream sub-chunk `cur`: slots [cur*K, min((cur+1)*K, E)), row by row
+        int64_t e = cur * kSubSlots;
+        const int64_t e_end = e + kSubSlots < E ? e + kSubSlots : E;
+        int64_t r = e / Vv;
+        while (e < e_end) {
+            const int64_t row_end = (r + 1) * Vv;
+            const int64_t seg_end = e_end < row_end ? e_end : row_end;
+            const int b = row_owner(cu_s, B, r);
+            const int64_t src = (int64_t)b * g1 + (r - cu_s[b]);
+            float best = -INFINITY;
+            int bidx = -1;
+            lane_row_segment<kVec, kStreamUnroll>(p.logits + (size_t)src * (size_t)p.V,
+                                                  e - r * Vv, seg_end - r * Vv, lane, best, bidx);
+            uint64_t key = bidx >= 0 ? argmax_key(best, (uint32_t)bidx) : 0ull;
+            key = wave_max_u64(key);
+            if (lane == 0) p.keys[cur + r] = key;
+            e = seg_end;
+            ++r;
         }
-        __syncthreads();
-        __atomic_signal_fence(__ATOMIC_SEQ_CST);  // key loads stay after the counts
-        const int nd = ndone_s;
-        for (int k = wave; k < nd; k += nw)
-            wave_accept_request<true>(p.keys, cu_s, p.tokens, done_s[k], g, total, Vv, Q, p.pam,
-                                      p.acc, p.bonus);
-        __syncthreads();
     }
+}
+
+// ----------------------------------------------------------------- finish
+
+template <bool kVec>
+__global__ __launch_bounds__(kFinishThreads) void step_finish_kernel(
+    const uint64_t *__restrict__ keys, const int32_t *__restrict__ cu,
+    const int32_t *__restrict__ tokens, int B, int gamma, int V, int32_t *__restrict__ pam,
+    int32_t *__restrict__ acc, int32_t *__restrict__ bonus) {
+    const int b = blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave;
+    if (b >= B) return;
+    const int total = packed_total(cu, B, B * (gamma + 1));
+    const int64_t Vv = kVec ? (V >> 3) : V;
+    wave_accept_request(keys, cu, tokens, b, gamma, total, Vv, kSubSlots, pam, acc, bonus);
 }
 
 // ----------------------------------------------------------------- launch
 
 template <bool kVec>
-static int back_grid(size_t lds) {
-    // resident workgroups of the back kernel for this LDS size, cached per
+static int stream_grid(size_t lds) {
+    // resident workgroups of the stream kernel for this LDS size, cached per
     // device and 4 KiB LDS bucket
     static std::atomic<int> cache[64][13];
     int dev = 0;
@@ -233,13 +186,12 @@ static int back_grid(size_t lds) {
     int gsz = cache[dev][bucket].load(std::memory_order_relaxed);
     if (gsz > 0) return gsz;
     int blocks = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, step_back_kernel<kVec>, kBackThreads,
-                                                     (size_t)bucket * 4096) != hipSuccess ||
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, step_stream_kernel<kVec>,
+                                                     kStreamThreads, (size_t)bucket * 4096) !=
+            hipSuccess ||
         blocks < 1)
         blocks = 1;
-    int64_t gg = (int64_t)blocks * device_cu_count();
-    if (gg * kBackWaves > kMaxWaves) gg = kMaxWaves / kBackWaves;
-    gsz = (int)gg;
+    gsz = blocks * device_cu_count();
     cache[dev][bucket].store(gsz, std::memory_order_relaxed);
     return gsz;
 }
@@ -250,12 +202,9 @@ hipError_t launch_fused_step(const uint16_t *hidden, const uint16_t *w, float bi
                              long long budget, float *conf, float *surv, int32_t *lengths,
                              int32_t *cu, int32_t *ptok, int32_t *psrc, int32_t *pam,
                              int32_t *acc, int32_t *bonus, void *ws, hipStream_t s) {
-    const int N = B * gamma;
     if (B > kMaxFusedB) return hipErrorNotSupported;
-    if (mode == DSPARK_CUT_BUDGET && N > kMaxFusedBudgetN) return hipErrorNotSupported;
     char *wsb = static_cast<char *>(ws);
     uint64_t *keys = reinterpret_cast<uint64_t *>(wsb + ws_keys_offset());
-    unsigned long long *cnt = reinterpret_cast<unsigned long long *>(wsb + ws_cnt_offset(B, gamma));
 
     const bool hvec = (d % 8 == 0) && (((uintptr_t)hidden | (uintptr_t)w) % 16 == 0);
     FrontParams fp;
@@ -270,7 +219,6 @@ hipError_t launch_fused_step(const uint16_t *hidden, const uint16_t *w, float bi
     fp.conf = conf;
     fp.surv = surv;
     fp.lengths = lengths;
-    fp.cnt = cnt;
     if (hvec && d <= kFrontMaxLdsW)
         hipLaunchKernelGGL((step_front_kernel<true, true>), dim3(B), dim3(kFrontThreads),
                            (size_t)d * 2, s, fp);
@@ -281,34 +229,35 @@ hipError_t launch_fused_step(const uint16_t *hidden, const uint16_t *w, float bi
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
 
+    if (mode == DSPARK_CUT_BUDGET) {
+        e = launch_schedule(surv, B, gamma, mode, cutoff, budget, lengths, s);
+        if (e != hipSuccess) return e;
+    }
+
     const bool vvec = (V % 8 == 0) && ((uintptr_t)logits % 16 == 0);
     const size_t lds = (size_t)(2 * B + 1) * sizeof(int);
-    BackParams p;
+    StreamParams p;
     p.logits = logits;
     p.tokens = tokens;
-    p.surv = surv;
+    p.lengths = lengths;
     p.B = B;
     p.gamma = gamma;
     p.V = V;
-    p.mode = mode;
-    p.t_eff = mode == DSPARK_CUT_BUDGET ? (int)(budget < (long long)N ? budget : N) : 0;
-    p.lengths = lengths;
     p.cu = cu;
     p.ptok = ptok;
     p.psrc = psrc;
-    p.pam = pam;
-    p.acc = acc;
-    p.bonus = bonus;
     p.keys = keys;
-    p.cnt = cnt;
+    const dim3 fgrid((B + kFinishThreads / kWave - 1) / (kFinishThreads / kWave));
     if (vvec) {
-        const int G = back_grid<true>(lds);
-        p.W = G * kBackWaves;
-        hipLaunchKernelGGL((step_back_kernel<true>), dim3(G), dim3(kBackThreads), lds, s, p);
+        hipLaunchKernelGGL((step_stream_kernel<true>), dim3(stream_grid<true>(lds)),
+                           dim3(kStreamThreads), lds, s, p);
+        hipLaunchKernelGGL((step_finish_kernel<true>), fgrid, dim3(kFinishThreads), 0, s, keys, cu,
+                           tokens, B, gamma, V, pam, acc, bonus);
     } else {
-        const int G = back_grid<false>(lds);
-        p.W = G * kBackWaves;
-        hipLaunchKernelGGL((step_back_kernel<false>), dim3(G), dim3(kBackThreads), lds, s, p);
+        hipLaunchKernelGGL((step_stream_kernel<false>), dim3(stream_grid<false>(lds)),
+                           dim3(kStreamThreads), lds, s, p);
+        hipLaunchKernelGGL((step_finish_kernel<false>), fgrid, dim3(kFinishThreads), 0, s, keys,
+                           cu, tokens, B, gamma, V, pam, acc, bonus);
     }
     return hipGetLastError();
 }
