@@ -88,6 +88,17 @@ def step_bytes(cfg, total: int) -> int:
     return reads + writes
 
 
+def step_bytes_a3_a6(cfg, total: int) -> int:
+    """Algorithmic HBM bytes of schedule + compact + accept given the survival
+    curves: survival and cutoffs in, the packed logit rows, tokens, and every
+    integer output."""
+    B, g, V = cfg.B, cfg.gamma, cfg.V
+    reads = (4 * B * g + (4 * B if cfg.mode == "threshold" else 0)
+             + 4 * B * (g + 1) + 2 * V * total)
+    writes = 4 * B + 4 * (B + 1) + 12 * total + 8 * B
+    return reads + writes
+
+
 def run_arm(cfg, slots, outs, ws, steps, warmup, dspark, torch):
     """Time `steps` dspark_step calls cycling over the resident slots."""
     R = len(slots)
@@ -126,6 +137,131 @@ def run_arm(cfg, slots, outs, ws, steps, warmup, dspark, torch):
                 step_ms_sorted=sorted(step_ms), totals=totals)
 
 
+def run_stage_arm(cfg, slots, outs, ws, steps, dspark, torch):
+    """Steps 3-6 through the stage entry points (dspark_schedule ->
+    dspark_compact without a logits copy -> dspark_accept on the dense logits
+    through packed_src_row), given the survival curves of a prior fused step."""
+    R = len(slots)
+    surv = [o["survival"].clone() for o in outs]
+
+    def launch(i):
+        s, o = slots[i % R], outs[i % R]
+        dspark.dspark_schedule(surv[i % R], cfg.mode, cutoff=s.cutoff, budget=cfg.budget,
+                               lengths=o["lengths"])
+        dspark.dspark_compact(o["lengths"], s.tokens, out=o)
+        dspark.dspark_accept(s.logits, o["packed_src_row"], o["cu_seqlens"], s.tokens, out=o, ws=ws)
+
+    for i in range(max(8, R)):
+        launch(i)
+    torch.cuda.synchronize()
+    totals = [int(o["cu_seqlens"][-1].item()) for o in outs]
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    for i in range(steps):
+        ev[i][0].record()
+        launch(i)
+        ev[i][1].record()
+    torch.cuda.synchronize()
+    ms = sorted(a.elapsed_time(b) for a, b in ev)
+    mean_ms = sum(ms) / steps
+    nbytes = sum(step_bytes_a3_a6(cfg, totals[i % R]) for i in range(steps)) / steps
+    return dict(event_ms_per_step=mean_ms, p50_ms=ms[steps // 2], bytes_a3_a6=nbytes,
+                achieved_gbs=nbytes / (mean_ms / 1e3) / 1e9,
+                frac_of_hbm_peak=nbytes / (mean_ms / 1e3) / 1e9 / HBM_PEAK_GBS)
+
+
+def stream_read_context(torch, dev):
+    """HBM GB/s of a plain device-to-device copy of 1 GiB on the same device,
+    for context (bytes read plus bytes written over the copy time)."""
+    src = torch.ones(1 << 30, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(2):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(5):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    gbs = 5 * 2 * src.numel() / (e0.elapsed_time(e1) / 1e3) / 1e9
+    del src, dst
+    return dict(kernel="device-to-device copy of 1 GiB (read + write bytes)", gbs=gbs,
+                frac_of_hbm_peak=gbs / HBM_PEAK_GBS)
+
+
+def _oracle_worker(args):
+    """One host process of the all-core oracle timing: whole oracle steps on the
+    shared batches until `seconds` have passed."""
+    import numpy as np
+    from multiprocessing import shared_memory
+
+    import oracle
+
+    specs, scalars, mode, seconds, wid = args
+    shms, arrs = [], []
+    for batch in specs:
+        a = {}
+        for name, (shm_name, shape, dtype) in batch.items():
+            shm = shared_memory.SharedMemory(name=shm_name)
+            shms.append(shm)
+            a[name] = np.ndarray(shape, dtype=dtype, buffer=shm.buf)
+        arrs.append(a)
+    rows = n = 0
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < seconds:
+        h, sc = arrs[(n + wid) % len(arrs)], scalars[(n + wid) % len(arrs)]
+        o = oracle.step(h["hidden"], h["w"], sc["bias"], h["temps"], h["tokens"], h["logits"],
+                        mode, cutoff=h["cutoff"], budget=sc["budget"])
+        rows += int(o["cu_seqlens"][-1])
+        n += 1
+    el = time.perf_counter() - t0
+    del arrs
+    for shm in shms:
+        shm.close()
+    return rows, n, el
+
+
+def cpu_baseline_all_cores(cfg, host, seconds=10.0):
+    """The same oracle in one process per host core (at most 16, the host share
+    of one GPU), each on the shared batches: aggregate packed rows/s."""
+    import multiprocessing as mp
+    from multiprocessing import shared_memory
+
+    import numpy as np
+
+    cores = max(1, min(16, os.cpu_count() or 1))
+    shms, specs, scalars = [], [], []
+    try:
+        for h in host:
+            spec = {}
+            for name in ("hidden", "w", "temps", "tokens", "cutoff", "logits"):
+                a = np.ascontiguousarray(h[name])
+                shm = shared_memory.SharedMemory(create=True, size=max(1, a.nbytes))
+                shms.append(shm)
+                np.ndarray(a.shape, dtype=a.dtype, buffer=shm.buf)[...] = a
+                spec[name] = (shm.name, a.shape, a.dtype.str)
+            specs.append(spec)
+            scalars.append(dict(bias=h["bias"], budget=h["budget"]))
+        ctx = mp.get_context("spawn")
+        t0 = time.perf_counter()
+        with ctx.Pool(cores) as pool:
+            res = pool.map(_oracle_worker, [(specs, scalars, cfg.mode, seconds, i)
+                                            for i in range(cores)])
+        wall = time.perf_counter() - t0
+    finally:
+        for shm in shms:
+            shm.close()
+            shm.unlink()
+    rows = sum(r[0] for r in res)
+    steps = sum(r[1] for r in res)
+    busy = max(r[2] for r in res)
+    return dict(value=rows / busy, unit="packed verify rows/s", cores=cores, kind="oracle",
+                sample=f"{cores} host processes x {seconds:.0f} s of whole oracle steps on the "
+                       f"same {len(host)} batches: {steps} steps, {rows} packed rows "
+                       f"(wall {wall:.1f} s including process start)")
+
+
 def arm_summary(cfg, r, steps, B):
     ev_s = r["mean_step_ms"] * steps / 1e3
     return dict(
@@ -134,6 +270,7 @@ def arm_summary(cfg, r, steps, B):
         ms_per_step=r["wall_s"] * 1e3 / steps,
         event_ms_per_step=r["mean_step_ms"],
         p10_ms=r["step_ms_sorted"][len(r["step_ms_sorted"]) // 10],
+        p50_ms=r["step_ms_sorted"][len(r["step_ms_sorted"]) // 2],
         p90_ms=r["step_ms_sorted"][(9 * len(r["step_ms_sorted"])) // 10],
         mean_packed_rows=r["rows"] / steps,
         achieved_gbs=r["bytes"] / ev_s / 1e9,
@@ -174,7 +311,7 @@ def cpu_baseline(cfg, slots, min_s=10.0, max_s=30.0):
     return dict(value=rows / el, unit="packed verify rows/s", cores=1, kind="oracle",
                 sample=f"{n} whole steps (batches 0-{len(host) - 1} of the rotation, "
                        f"{rows} packed rows) of the same workload in {el:.1f} s",
-                seconds=el), results
+                seconds=el), results, host
 
 
 def check_against_oracle(results, outs):
@@ -203,6 +340,8 @@ def main():
     ap.add_argument("--rotation", type=int, default=8)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra-arms", action="store_true")
+    ap.add_argument("--no-all-cores", action="store_true",
+                    help="skip the oracle timing on all host cores")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a 1 GiB device-to-device copy (a plain copy kernel of known "
                          "size) so counter runs can scale FETCH_SIZE / WRITE_SIZE")
@@ -238,7 +377,12 @@ def main():
         f"{s_t['achieved_gbs']:.0f} GB/s ({100 * s_t['frac_of_hbm_peak']:.1f} % of peak)")
 
     extra = {}
+    context = None
     if not args.no_extra_arms:
+        st = run_stage_arm(cfg_t, slots, outs, ws, args.steps, dspark, torch)
+        extra["stages_a3_a6_threshold"] = st
+        log(f"stage path a3-a6: {st['event_ms_per_step'] * 1e3:.1f} us/step, "
+            f"{st['achieved_gbs']:.0f} GB/s")
         # budget arm on the same resident batches (the two arms share their seeds)
         r_b = run_arm(cfg_b, slots, outs, ws, args.steps, args.warmup, dspark, torch)
         extra["mixed_budget_T742"] = arm_summary(cfg_b, r_b, args.steps, cfg_b.B)
@@ -251,12 +395,16 @@ def main():
         r_4 = run_arm(cfg4, slots4, outs4, ws4, args.steps, args.warmup, dspark, torch)
         extra["budget_d7168_V129280_T768"] = arm_summary(cfg4, r_4, args.steps, cfg4.B)
         log(f"budget d=7168 arm: {extra['budget_d7168_V129280_T768']['rows_per_s']:.3e} rows/s")
+        del slots4, outs4
+        context = stream_read_context(torch, dev)
+        log(f"plain device copy: {context['gbs']:.0f} GB/s")
 
     cpu = None
+    cpu_all = None
     parity = None
     if not args.no_cpu_baseline:
         log("timing the oracle on the host (bounded sample)")
-        cpu, results = cpu_baseline(cfg_t, slots)
+        cpu, results, host = cpu_baseline(cfg_t, slots)
         # the GPU outputs of the first timed batches: rerun them once more to be sure the
         # buffers hold exactly those batches' results
         for i in range(len(results)):
@@ -267,6 +415,11 @@ def main():
         parity = check_against_oracle(results, outs[: len(results)])
         cpu.pop("seconds", None)
         log(f"oracle: {cpu['value']:.1f} rows/s on 1 core; parity on sampled batches: {parity}")
+        if not args.no_all_cores:
+            log("timing the oracle on all host cores (bounded sample)")
+            cpu_all = cpu_baseline_all_cores(cfg_t, host)
+            log(f"oracle: {cpu_all['value']:.1f} rows/s on {cpu_all['cores']} cores")
+        del host
 
     if args.calibrate_copy:
         src = torch.empty(1 << 30, dtype=torch.uint8, device=dev).fill_(1)
@@ -299,8 +452,11 @@ def main():
                    "mean_packed_rows": s_t["mean_packed_rows"]},
         "request_steps_per_s": s_t["request_steps_per_s"],
         "achieved_gbs": s_t["achieved_gbs"],
+        "step_us": {"mean": r_t["mean_step_ms"] * 1e3,
+                    "p10": s_t["p10_ms"] * 1e3, "p50": s_t["p50_ms"] * 1e3,
+                    "p90": s_t["p90_ms"] * 1e3},
         "roofline": {"bound": "hbm",
-                     "kernel": "dspark_step = step_front_kernel + step_stream_kernel + step_finish_kernel (one stream; budget mode adds schedule_budget_kernel)",
+                     "kernel": "dspark_step = step_front_kernel + step_stream_kernel (one stream)",
                      "achieved": mean_bytes / (r_t["mean_step_ms"] / 1e3) / 1e9,
                      "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": mean_bytes / (r_t["mean_step_ms"] / 1e3) / 1e9 / HBM_PEAK_GBS,
@@ -308,6 +464,8 @@ def main():
                      "algorithmic_bytes_per_launch": mean_bytes,
                      "mean_launch_us": r_t["mean_step_ms"] * 1e3},
         "cpu_baseline": cpu,
+        "cpu_baseline_all_cores": cpu_all,
+        "stream_read_context": context,
         "parity_on_sampled_batches": parity,
         "arms": extra,
     }

@@ -115,45 +115,48 @@ __device__ __forceinline__ uint64_t load_key_coherent(const uint64_t *p) {
 }
 
 // Argmax of packed row r from the keys of the waves whose shares touch it.
-// kCoherent: the keys were written by this same kernel.
+// kCoherent: the keys were written by this same kernel. The key loads are
+// issued four at a time, so a row costs one memory round trip in the usual
+// case of at most four segments.
 template <bool kCoherent = false>
 __device__ __forceinline__ int32_t row_argmax(const uint64_t *__restrict__ keys, int64_t r,
                                               int64_t Vv, int64_t Q) {
     const int64_t w_lo = (r * Vv) / Q;
     const int64_t w_hi = ((r + 1) * Vv - 1) / Q;
     uint64_t k = 0;
-    for (int64_t w = w_lo; w <= w_hi; ++w) {
-        const uint64_t x = kCoherent ? load_key_coherent(keys + w + r) : keys[w + r];
-        k = x > k ? x : k;
+    for (int64_t w = w_lo; w <= w_hi; w += 4) {
+        uint64_t x[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int64_t i = w + u <= w_hi ? w + u + r : w_lo + r;  // in range, repeats are harmless
+            x[u] = kCoherent ? load_key_coherent(keys + i) : keys[i];
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) k = x[u] > k ? x[u] : k;
     }
     return key_index(k);
 }
 
-// Acceptance and bonus of request b by one wave: lane j handles packed row
-// cu[b] + j (chunks of 64 rows). The first row j where the target disagrees
-// with draft j+1, or j = L_b, is the accepted count; its argmax is the bonus.
-template <bool kCoherent = false>
-__device__ __forceinline__ void wave_accept_request(const uint64_t *__restrict__ keys,
-                                                    const int32_t *__restrict__ cu,
-                                                    const int32_t *__restrict__ tokens, int b,
-                                                    int gamma, int total, int64_t Vv, int64_t Q,
-                                                    int32_t *__restrict__ pam,
-                                                    int32_t *__restrict__ acc,
-                                                    int32_t *__restrict__ bonus) {
+// Acceptance and bonus of one request by one wave, from its verified rows'
+// argmax: row_am(j) for j in [0, n), n = L_b + 1 rows (root first). Lane j
+// handles row j (chunks of 64 rows) and stores it at pam_b[j]. The first row j
+// where the target disagrees with draft j+1, or j = L_b, is the accepted
+// count; that row's argmax is the bonus. n <= 0 gives accepted 0, bonus -1.
+template <typename RowAm>
+__device__ __forceinline__ void wave_accept_rows(RowAm row_am, int n, int gamma,
+                                                 const int32_t *__restrict__ tok,
+                                                 int32_t *__restrict__ pam_b,
+                                                 int32_t *__restrict__ acc_b,
+                                                 int32_t *__restrict__ bonus_b) {
     const int lane = threadIdx.x & (kWave - 1);
-    int start = cu[b], end = cu[b + 1];
-    start = start < 0 ? 0 : (start > total ? total : start);
-    end = end < start ? start : (end > total ? total : end);
-    const int n = end - start;
     if (n <= 0) {
         if (lane == 0) {
-            acc[b] = 0;
-            bonus[b] = -1;
+            *acc_b = 0;
+            *bonus_b = -1;
         }
         return;
     }
     const int L = n - 1 < gamma ? n - 1 : gamma;
-    const int32_t *tok = tokens + (size_t)b * (gamma + 1);
     int a = -1;
     int32_t bon = -1;
     for (int j0 = 0; j0 < n; j0 += kWave) {
@@ -161,8 +164,8 @@ __device__ __forceinline__ void wave_accept_request(const uint64_t *__restrict__
         int32_t am = -1;
         bool stop = false;
         if (j < n) {
-            am = row_argmax<kCoherent>(keys, start + j, Vv, Q);
-            pam[start + j] = am;
+            am = row_am(j);
+            pam_b[j] = am;
             stop = (j >= L) || (am != tok[j + 1]);
         }
         const uint64_t mask = __ballot(stop);
@@ -173,9 +176,27 @@ __device__ __forceinline__ void wave_accept_request(const uint64_t *__restrict__
         }
     }
     if (lane == 0) {
-        acc[b] = a;
-        bonus[b] = bon;
+        *acc_b = a;
+        *bonus_b = bon;
     }
+}
+
+// Acceptance and bonus of request b when every packed row's argmax comes from
+// segment keys (packed row r = cu[b] + j).
+template <bool kCoherent = false>
+__device__ __forceinline__ void wave_accept_request(const uint64_t *__restrict__ keys,
+                                                    const int32_t *__restrict__ cu,
+                                                    const int32_t *__restrict__ tokens, int b,
+                                                    int gamma, int total, int64_t Vv, int64_t Q,
+                                                    int32_t *__restrict__ pam,
+                                                    int32_t *__restrict__ acc,
+                                                    int32_t *__restrict__ bonus) {
+    int start = cu[b], end = cu[b + 1];
+    start = start < 0 ? 0 : (start > total ? total : start);
+    end = end < start ? start : (end > total ? total : end);
+    wave_accept_rows([&](int j) { return row_argmax<kCoherent>(keys, start + j, Vv, Q); },
+                     end - start, gamma, tokens + (size_t)b * (gamma + 1), pam + start, acc + b,
+                     bonus + b);
 }
 
 }  // namespace dspark

@@ -78,7 +78,7 @@ DSPARK_API const char *dspark_status_string(int status) {
 
 DSPARK_API size_t dspark_workspace_bytes(int B, int gamma, int V) {
     if (check_bg(B, gamma) != DSPARK_OK || V < 1) return 0;
-    return ws_total_bytes(B, gamma, V);
+    return ws_total_bytes(B, gamma);
 }
 
 DSPARK_API dspark_status dspark_workspace_init(void *ws, size_t ws_bytes, void *stream) {
@@ -148,7 +148,7 @@ DSPARK_API dspark_status dspark_accept(const dspark_bf16 *logits, const int32_t 
         misaligned(tokens, 4) || misaligned(packed_argmax, 4) || misaligned(accepted, 4) ||
         misaligned(bonus, 4) || misaligned(ws, 16))
         return DSPARK_ERR_ALIGN;
-    if (ws_bytes < ws_total_bytes(B, gamma, V)) return DSPARK_ERR_WORKSPACE;
+    if (ws_bytes < ws_total_bytes(B, gamma)) return DSPARK_ERR_WORKSPACE;
     return launched(launch_accept(logits, packed_src_row, cu_seqlens, tokens, B, gamma, V,
                                   packed_argmax, accepted, bonus, ws, as_stream(stream)));
 }
@@ -177,11 +177,11 @@ DSPARK_API dspark_status dspark_step(const dspark_bf16 *hidden, const dspark_bf1
         misaligned(packed_src_row, 4) || misaligned(packed_argmax, 4) ||
         misaligned(accepted, 4) || misaligned(bonus, 4) || misaligned(ws, 16))
         return DSPARK_ERR_ALIGN;
-    if (ws_bytes < ws_total_bytes(B, gamma, V)) return DSPARK_ERR_WORKSPACE;
+    if (ws_bytes < ws_total_bytes(B, gamma)) return DSPARK_ERR_WORKSPACE;
     hipStream_t s = as_stream(stream);
     char *wsb = static_cast<char *>(ws);
-    float *surv = survival ? survival : reinterpret_cast<float *>(wsb + ws_surv_offset(B, gamma, V));
-    float *cf = conf ? conf : reinterpret_cast<float *>(wsb + ws_conf_offset(B, gamma, V));
+    float *surv = survival ? survival : reinterpret_cast<float *>(wsb + ws_surv_offset(B, gamma));
+    float *cf = conf ? conf : reinterpret_cast<float *>(wsb + ws_conf_offset(B, gamma));
     hipError_t e = launch_fused_step(hidden, w, bias, temps, tokens, logits, B, gamma, d, V, mode,
                                      cutoff, budget, cf, surv, lengths, cu_seqlens, packed_tokens,
                                      packed_src_row, packed_argmax, accepted, bonus, ws, s);

@@ -75,30 +75,49 @@ __device__ __forceinline__ int64_t partition_q(int64_t E, int64_t W) {
     return q < kMinSlotsPerWave ? kMinSlotsPerWave : q;
 }
 
+// ---------------------------------------------------- fused-step sub-chunks
+// The fused step streams a virtual array of E vector slots (rows laid end to
+// end) in sub-chunks of K slots, K = max(kSubMin, ceil(E / Wt)) for a target
+// wave count Wt: about one contiguous sub-chunk per wave. Sub-chunk s stores
+// the key of its segment inside row r at keys[s + r], collision-free as for
+// the balanced partition, with s < Wt <= kMaxWaves.
+constexpr int64_t kSubMin = 1024;  // 16 KiB of bf16
+
+__device__ __forceinline__ int64_t sub_len(int64_t E, int64_t Wt) {
+    const int64_t k = (E + Wt - 1) / Wt;
+    return k < kSubMin ? kSubMin : k;
+}
+
 // ------------------------------------------------------------ workspace map
-// keys:  uint64 [key_slots(B,gamma,V)] argmax segment keys
+// ctrl:  [0, 256)                arrival counter of the fused step's front
+//                                workgroups (uint32 at offset 0); zero between
+//                                calls, at the same place for every size, so
+//                                one workspace serves calls of any size it is
+//                                large enough for
+// rcnt:  uint64 [kMaxFusedB]     per-request arrival counters of the fused
+//                                step's stream kernel (zeroed by its front)
+// keys:  uint64 [kMaxWaves + B*(gamma+1)] argmax segment keys of packed rows
+// rkeys: uint64 [kMaxWaves + B]  segment keys of the root rows (fused step)
 // surv:  float [B*gamma]         survival scratch (when the caller passes none)
 // conf:  float [B*gamma]         score scratch (when the caller passes none)
-constexpr int64_t kMaxWaves = 16384;   // resident waves of the static argmax grid
-constexpr int64_t kSubSlots = 1024;    // 16-byte slots per fused-step sub-chunk (16 KiB)
+constexpr int64_t kMaxWaves = 16384;  // bound on waves (or sub-chunks) per pass
+constexpr int kMaxFusedB = 4096;      // largest batch of the fused step
+constexpr size_t kCtrlBytes = 256;
 
-// Key slots: the stage argmax keeps one key per (wave, row) segment (index
-// w + r, w < kMaxWaves); the fused step one per (sub-chunk, row) segment
-// (index s + r). Sized for the scalar layout (one bf16 per slot), the larger.
-inline int64_t key_slots(int64_t B, int64_t gamma, int64_t V) {
-    const int64_t cap = B * (gamma + 1);
-    const int64_t sub = (cap * V + kSubSlots - 1) / kSubSlots;
-    return (sub > kMaxWaves ? sub : kMaxWaves) + cap;
+inline size_t ws_ctrl_offset() { return 0; }
+inline size_t ws_rcnt_offset() { return kCtrlBytes; }
+inline size_t ws_keys_offset() { return kCtrlBytes + (size_t)8 * kMaxFusedB; }
+inline size_t ws_rkeys_offset(int64_t B, int64_t gamma) {
+    return ws_keys_offset() + (size_t)8 * (size_t)(kMaxWaves + B * (gamma + 1));
 }
-inline size_t ws_keys_offset() { return 0; }
-inline size_t ws_surv_offset(int64_t B, int64_t gamma, int64_t V) {
-    return ws_keys_offset() + (size_t)8 * (size_t)key_slots(B, gamma, V);
+inline size_t ws_surv_offset(int64_t B, int64_t gamma) {
+    return ws_rkeys_offset(B, gamma) + (size_t)8 * (size_t)(kMaxWaves + B);
 }
-inline size_t ws_conf_offset(int64_t B, int64_t gamma, int64_t V) {
-    return ws_surv_offset(B, gamma, V) + (size_t)4 * (size_t)(B * gamma);
+inline size_t ws_conf_offset(int64_t B, int64_t gamma) {
+    return ws_surv_offset(B, gamma) + (size_t)4 * (size_t)(B * gamma);
 }
-inline size_t ws_total_bytes(int64_t B, int64_t gamma, int64_t V) {
-    size_t s = ws_conf_offset(B, gamma, V) + (size_t)4 * (size_t)(B * gamma);
+inline size_t ws_total_bytes(int64_t B, int64_t gamma) {
+    const size_t s = ws_conf_offset(B, gamma) + (size_t)4 * (size_t)(B * gamma);
     return (s + 255) & ~(size_t)255;
 }
 

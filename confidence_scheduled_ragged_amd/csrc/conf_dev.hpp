@@ -12,6 +12,8 @@
 
 namespace dspark {
 
+constexpr int kGemvUnroll = 4;  // 16-byte hidden loads in flight per lane
+
 // One wave per hidden row: z[i] = sum_k w[k]*h[b,i,k] + bias for the gamma rows
 // of one request. hidden_b points at row 0 of the request. kVec: d % 8 == 0
 // and both pointers 16-byte aligned, so each lane loads 8 bf16 per access.
@@ -32,16 +34,16 @@ __device__ __forceinline__ void request_logits(const uint16_t *__restrict__ hidd
             const u32x4 *w4 = reinterpret_cast<const u32x4 *>(w);
             const int nv = d >> 3;
             int v = lane;
-            // four vectors per lane in flight per trip
-            for (; v + 3 * kWave < nv; v += 4 * kWave) {
-                u32x4 hv[4], wv[4];
+            // kGemvUnroll vectors per lane in flight per trip
+            for (; v + (kGemvUnroll - 1) * kWave < nv; v += kGemvUnroll * kWave) {
+                u32x4 hv[kGemvUnroll], wv[kGemvUnroll];
 #pragma unroll
-                for (int u = 0; u < 4; ++u) {
+                for (int u = 0; u < kGemvUnroll; ++u) {
                     hv[u] = __builtin_nontemporal_load(h4 + v + u * kWave);
                     wv[u] = w4[v + u * kWave];
                 }
 #pragma unroll
-                for (int u = 0; u < 4; ++u) {
+                for (int u = 0; u < kGemvUnroll; ++u) {
 #pragma unroll
                     for (int c = 0; c < 4; ++c) {
                         acc = fmaf(bf16_lo(hv[u][c]), bf16_lo(wv[u][c]), acc);

@@ -1,24 +1,27 @@
-// fused.hip - the whole verify step as a short chain of launches on one stream.
+// fused.hip - the whole verify step as two launches on one stream.
 //
-//   front   one workgroup per request: the confidence GEMV of the request's gamma
-//           hidden rows (one wave per row), the STS sigmoid, the sequential
-//           survival product and, in threshold mode, the verify length.
-//   select  (budget mode only) one workgroup: the batch-wide top-T pick over all
-//           survival values and each request's verify length.
-//   stream  a persistent grid: every workgroup scans the verify lengths into
-//           cu_seqlens in LDS and writes the schedule outputs of its own
-//           requests; then the packed logit rows of all requests, laid end to
-//           end and cut into 16 KiB sub-chunks, are streamed: each wave leaves
-//           one argmax key per row segment of each sub-chunk it reads. The
-//           sub-chunks are dealt out cyclically over all resident waves.
-//   finish  one wave per request: each packed row's argmax from its keys, the
-//           longest agreeing prefix and the bonus token.
+//   front   two kinds of workgroup in one grid. Workgroup b < B: the confidence
+//           GEMV of request b's gamma hidden rows, the STS sigmoid, the
+//           sequential survival product and, in threshold mode, the verify
+//           length. The other workgroups stream the root rows (row 0 of every
+//           request, verified whatever the cut) while the GEMV runs, and leave
+//           argmax keys of their segments. In budget mode the last request
+//           workgroup to finish (counted on an atomic arrival counter, no
+//           waiting) runs the batch-wide top-T pick and writes every length.
+//   stream  every workgroup scans the verify lengths into cu_seqlens in LDS and
+//           writes the schedule outputs of its own requests; then the draft
+//           rows of all requests, laid end to end, are cut into sub-chunks of
+//           about equal length, one contiguous run per wave, and each wave
+//           leaves one argmax key per row segment. A per-request atomic counts
+//           the draft slots done; the wave that completes a request merges its
+//           keys and writes the acceptance and bonus token (no waiting).
 //
-// Small cyclic sub-chunks spread the rows of every request over the whole
-// chip. Dynamic hand-out through per-XCD atomic work queues was measured
-// slower: one queue serves about one ticket per 11 ns, and even a queue that
-// serves only the last fifth of the sub-chunks cost 2-6 us per step. Grid-wide
-// waits were measured at 16-76 us each and are not used.
+// Long contiguous runs per wave were measured faster than small interleaved
+// sub-chunks (HBM row-buffer locality), and two 16-byte loads in flight per
+// lane with full occupancy faster than deeper unrolling with fewer waves.
+// Dynamic hand-out through per-XCD atomic work queues was measured slower:
+// one queue address serves about one ticket per 11-15 ns. Grid-wide waits
+// were measured at 16-76 us each and are not used.
 //
 // [P1] "DFlash to DSpark in SGLang", sections "DSpark: a sequential head and a
 // verify budget" (head, survival, cut), "Ragged verify under full CUDA graphs"
@@ -33,41 +36,129 @@
 
 namespace dspark {
 
-constexpr int kFrontThreads = 1024;
+constexpr int kFrontThreads = 512;
 constexpr int kFrontMaxLdsW = 16384;
+constexpr int kFusedSelPer = 8;  // survival values per thread of the in-front select
+constexpr int kFusedSelMax = kFusedSelPer * kFrontThreads;
+constexpr int kFrontRootWGsPerCU = 1;  // root-row workgroups of the front grid per CU
 constexpr int kStreamThreads = 512;
-constexpr int kStreamUnroll = 8;
-constexpr int kFinishThreads = 256;
-constexpr int kMaxFusedB = 4096;  // LDS of the stream kernel: 8*B + 4 bytes
+constexpr int kStreamWavesPerCU = 16;  // target waves of the draft-row stream per CU
+constexpr int kStreamUnroll = 2;  // 16-byte loads in flight per lane (more waves, fewer bytes each)
 
 // ------------------------------------------------------------------ front
 
 struct FrontParams {
-    const uint16_t *hidden, *w;
+    const uint16_t *hidden, *w, *logits;
     const float *temps, *cutoff;
     float bias;
-    int gamma, d, mode;
+    int B, gamma, d, V, mode;
+    int t;                // budget mode: number of positions to pick, in [0, B*gamma]
     float *conf, *surv;
     int32_t *lengths;
+    uint64_t *rkeys;      // segment keys of the root rows
+    uint64_t *req_arrivals;  // [B] the stream kernel's per-request counters, zeroed here
+    unsigned *arrivals;   // budget select in the front kernel: arrival counter, else NULL
 };
 
-template <bool kVecH, bool kLdsW>
+// Root rows (dense row b*(gamma+1) of every request b), laid end to end and
+// cut into sub-chunks of about equal length, one per root wave: wave w of
+// nwaves streams sub-chunks w, w + nwaves, ... and leaves one key per row
+// segment at rkeys[s + b].
+template <bool kVec>
+__device__ __forceinline__ void front_root_rows(const FrontParams &p, int64_t w, int64_t nwaves) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const int64_t Vv = kVec ? (p.V >> 3) : p.V;
+    const int64_t E = (int64_t)p.B * Vv;
+    const int64_t K = sub_len(E, nwaves);
+    const int64_t NS = (E + K - 1) / K;
+    const size_t row_stride = (size_t)(p.gamma + 1) * (size_t)p.V;
+    for (int64_t cur = w; cur < NS; cur += nwaves) {
+        int64_t e = cur * K;
+        const int64_t e_end = e + K < E ? e + K : E;
+        int64_t r = e / Vv;
+        while (e < e_end) {
+            const int64_t row_end = (r + 1) * Vv;
+            const int64_t seg_end = e_end < row_end ? e_end : row_end;
+            float best = -INFINITY;
+            int bidx = -1;
+            lane_row_segment<kVec, kStreamUnroll>(p.logits + (size_t)r * row_stride, e - r * Vv,
+                                                  seg_end - r * Vv, lane, best, bidx);
+            uint64_t key = bidx >= 0 ? argmax_key(best, (uint32_t)bidx) : 0ull;
+            key = wave_max_u64(key);
+            if (lane == 0) p.rkeys[cur + r] = key;
+            e = seg_end;
+            ++r;
+        }
+    }
+}
+
+template <bool kVecH, bool kLdsW, bool kVecV>
 __global__ __launch_bounds__(kFrontThreads) void step_front_kernel(FrontParams p) {
-    extern __shared__ __align__(16) uint16_t w_lds[];
+    extern __shared__ __align__(16) uint16_t dyn_lds[];
     __shared__ float z_s[DSPARK_MAX_GAMMA], p_s[DSPARK_MAX_GAMMA], s_s[DSPARK_MAX_GAMMA];
+    __shared__ uint32_t hist[256], sh[2];
+    __shared__ int scan_lds[17];
+    __shared__ int last_s;
+    if ((int)blockIdx.x >= p.B) {
+        const int nw = blockDim.x / kWave;
+        front_root_rows<kVecV>(p, (int64_t)((int)blockIdx.x - p.B) * nw + threadIdx.x / kWave,
+                               (int64_t)((int)gridDim.x - p.B) * nw);
+        return;
+    }
     const int b = blockIdx.x;
+    const int tid = threadIdx.x, bd = blockDim.x;
+    if (tid == 0)
+        __hip_atomic_store(p.req_arrivals + b, (uint64_t)0, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
     const uint16_t *wp = p.w;
     if (kLdsW) {
-        stage_w(p.w, p.d, w_lds);
+        stage_w(p.w, p.d, dyn_lds);
         __syncthreads();
-        wp = w_lds;
+        wp = dyn_lds;
     }
     request_logits<kVecH>(p.hidden + (size_t)b * p.gamma * p.d, wp, p.bias, p.gamma, p.d, z_s);
     __syncthreads();
-    request_survival(z_s, p.temps, p.gamma, p_s, s_s, p.conf + (size_t)b * p.gamma,
-                     p.surv + (size_t)b * p.gamma);
-    if (threadIdx.x == 0 && p.mode == DSPARK_CUT_THRESHOLD)
-        p.lengths[b] = threshold_length(s_s, p.gamma, p.cutoff[b]);
+    request_survival(z_s, p.temps, p.gamma, p_s, s_s, p.conf + (size_t)b * p.gamma, nullptr);
+    const bool select_here = p.arrivals != nullptr;
+    float *surv_b = p.surv + (size_t)b * p.gamma;
+    for (int i = tid; i < p.gamma; i += bd) {
+        // the select reads survival from another workgroup of this grid: write
+        // it through to the device coherence point
+        if (select_here)
+            __hip_atomic_store(surv_b + i, s_s[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        else
+            surv_b[i] = s_s[i];
+    }
+    if (p.mode == DSPARK_CUT_THRESHOLD) {
+        if (tid == 0) p.lengths[b] = threshold_length(s_s, p.gamma, p.cutoff[b]);
+        return;
+    }
+    if (!select_here) return;
+
+    // budget: count this request as done once its survival stores are complete;
+    // the workgroup that counts the last request picks for the whole batch
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (tid == 0) {
+        const unsigned old = __hip_atomic_fetch_add(p.arrivals, 1u, __ATOMIC_RELAXED,
+                                                    __HIP_MEMORY_SCOPE_AGENT);
+        last_s = old == (unsigned)(p.B - 1);
+    }
+    __syncthreads();
+    if (!last_s) return;
+    if (tid == 0) __hip_atomic_store(p.arrivals, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const int N = p.B * p.gamma;
+    float *sv = reinterpret_cast<float *>(dyn_lds);  // w is no longer needed
+    __syncthreads();
+    for (int f = tid; f < N; f += bd)
+        sv[f] = __hip_atomic_load(p.surv + f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
+    if (p.t <= 0 || p.t >= N) {
+        for (int r = tid; r < p.B; r += bd) p.lengths[r] = p.t <= 0 ? 0 : p.gamma;
+        return;
+    }
+    const BudgetCut cut = budget_select_runs<kFusedSelPer>(sv, N, p.t, hist, sh);
+    budget_lengths(sv, p.B, p.gamma, cut, p.lengths, scan_lds);
 }
 
 // ----------------------------------------------------------------- stream
@@ -77,17 +168,22 @@ struct StreamParams {
     const int32_t *tokens;
     const int32_t *lengths;
     int B, gamma, V;
-    int32_t *cu, *ptok, *psrc;
+    int32_t *cu, *ptok, *psrc, *pam, *acc, *bonus;
     uint64_t *keys;
+    const uint64_t *rkeys;  // root-row keys from the front kernel
+    uint64_t *arrivals;     // [B] draft slots streamed per request, zeroed by the front
+    int target_waves;       // sub-chunk length: about one sub-chunk per target wave
+    int root_waves;         // waves that streamed the root rows in the front kernel
 };
 
-// Largest b in [0, B] with cu[b] <= r (cu non-decreasing, cu[0] = 0 <= r):
-// the request that owns packed row r when r < cu[B].
-__device__ __forceinline__ int row_owner(const int *cu, int B, int64_t r) {
+// Largest b in [0, B] with cu[b] - b <= r, i.e. the request that owns draft
+// row r (draft rows start at cu[b] - b; requests without drafts own none)
+// when r < cu[B] - B.
+__device__ __forceinline__ int draft_owner(const int *cu, int B, int64_t r) {
     int lo = 0, hi = B;
     while (lo < hi) {
         const int mid = (lo + hi + 1) >> 1;
-        if ((int64_t)cu[mid] <= r) lo = mid; else hi = mid - 1;
+        if ((int64_t)(cu[mid] - mid) <= r) lo = mid; else hi = mid - 1;
     }
     return lo;
 }
@@ -130,47 +226,74 @@ __global__ __launch_bounds__(kStreamThreads) void step_stream_kernel(StreamParam
         }
     }
 
-    // sub-chunks of the packed rows, dealt out cyclically: wave w of W streams
-    // sub-chunks w, w + W, w + 2W, ... (no atomics, no waits)
+    // draft rows in sub-chunks of about equal length, one per target wave,
+    // dealt out cyclically: wave w of W streams sub-chunks w, w + W, ...
+    // Long contiguous runs per wave keep the HBM row buffers better used than
+    // many short interleaved ones.
     const int64_t Vv = kVec ? (p.V >> 3) : p.V;
-    const int64_t E = (int64_t)cu_s[B] * Vv;
-    const int64_t NS = (E + kSubSlots - 1) / kSubSlots;
+    const int64_t E = (int64_t)(cu_s[B] - B) * Vv;
+    const int64_t K = sub_len(E, p.target_waves);
+    const int64_t Kr = sub_len((int64_t)B * Vv, p.root_waves);
+    const int64_t NS = (E + K - 1) / K;
     const int64_t W = (int64_t)gridDim.x * (bd / kWave);
+
+    // acceptance and bonus of request b by the calling wave: the root row's
+    // argmax from the front kernel's keys, the draft rows' from this kernel's
+    auto accept = [&](int b) {
+        const int start = cu_s[b];
+        const int dstart = start - b;  // first draft row of request b
+        wave_accept_rows(
+            [&](int j) {
+                return j == 0 ? row_argmax(p.rkeys, b, Vv, Kr)
+                              : row_argmax<true>(p.keys, dstart + j - 1, Vv, K);
+            },
+            len_s[b] + 1, g, p.tokens + (size_t)b * g1, p.pam + start, p.acc + b, p.bonus + b);
+    };
+    // requests without draft rows are finished by the workgroup that owns them
+    if (tid < kWave)
+        for (int b = blockIdx.x; b < B; b += gridDim.x)
+            if (len_s[b] == 0) accept(b);
+    // `n` more draft slots of request b are done and their keys stored: count
+    // them; the wave that completes the request finishes it (no waiting)
+    auto arrive = [&](int b, int64_t n) {
+        __builtin_amdgcn_s_waitcnt(0);  // the key stores are at the coherence point
+        unsigned long long old = 0;
+        if (lane == 0)
+            old = __hip_atomic_fetch_add(p.arrivals + b, (uint64_t)n, __ATOMIC_RELAXED,
+                                         __HIP_MEMORY_SCOPE_AGENT);
+        old = __shfl(old, 0, kWave);
+        if ((int64_t)old + n == (int64_t)len_s[b] * Vv) accept(b);
+    };
     for (int64_t cur = (int64_t)blockIdx.x * (bd / kWave) + tid / kWave; cur < NS; cur += W) {
         // stream sub-chunk `cur`: slots [cur*K, min((cur+1)*K, E)), row by row
-        int64_t e = cur * kSubSlots;
-        const int64_t e_end = e + kSubSlots < E ? e + kSubSlots : E;
+        int64_t e = cur * K;
+        const int64_t e_end = e + K < E ? e + K : E;
         int64_t r = e / Vv;
+        int cur_b = -1;    // request of the rows being streamed
+        int64_t done = 0;  // its slots streamed in this sub-chunk
         while (e < e_end) {
             const int64_t row_end = (r + 1) * Vv;
             const int64_t seg_end = e_end < row_end ? e_end : row_end;
-            const int b = row_owner(cu_s, B, r);
-            const int64_t src = (int64_t)b * g1 + (r - cu_s[b]);
+            const int b = draft_owner(cu_s, B, r);
+            if (b != cur_b) {
+                if (cur_b >= 0) arrive(cur_b, done);
+                cur_b = b;
+                done = 0;
+            }
+            const int64_t src = (int64_t)b * g1 + 1 + (r - (cu_s[b] - b));
             float best = -INFINITY;
             int bidx = -1;
             lane_row_segment<kVec, kStreamUnroll>(p.logits + (size_t)src * (size_t)p.V,
                                                   e - r * Vv, seg_end - r * Vv, lane, best, bidx);
             uint64_t key = bidx >= 0 ? argmax_key(best, (uint32_t)bidx) : 0ull;
             key = wave_max_u64(key);
-            if (lane == 0) p.keys[cur + r] = key;
+            if (lane == 0) store_key_coherent(p.keys + cur + r, key);
+            done += seg_end - e;
             e = seg_end;
             ++r;
         }
+        if (cur_b >= 0) arrive(cur_b, done);
     }
-}
-
-// ----------------------------------------------------------------- finish
-
-template <bool kVec>
-__global__ __launch_bounds__(kFinishThreads) void step_finish_kernel(
-    const uint64_t *__restrict__ keys, const int32_t *__restrict__ cu,
-    const int32_t *__restrict__ tokens, int B, int gamma, int V, int32_t *__restrict__ pam,
-    int32_t *__restrict__ acc, int32_t *__restrict__ bonus) {
-    const int b = blockIdx.x * (blockDim.x / kWave) + threadIdx.x / kWave;
-    if (b >= B) return;
-    const int total = packed_total(cu, B, B * (gamma + 1));
-    const int64_t Vv = kVec ? (V >> 3) : V;
-    wave_accept_request(keys, cu, tokens, b, gamma, total, Vv, kSubSlots, pam, acc, bonus);
 }
 
 // ----------------------------------------------------------------- launch
@@ -196,6 +319,18 @@ static int stream_grid(size_t lds) {
     return gsz;
 }
 
+template <bool kVecV>
+static void launch_front(bool hvec, bool ldsw, const FrontParams &fp, int root_wgs, size_t lds,
+                         hipStream_t s) {
+    const dim3 grid(fp.B + root_wgs), block(kFrontThreads);
+    if (hvec && ldsw)
+        hipLaunchKernelGGL((step_front_kernel<true, true, kVecV>), grid, block, lds, s, fp);
+    else if (hvec)
+        hipLaunchKernelGGL((step_front_kernel<true, false, kVecV>), grid, block, lds, s, fp);
+    else
+        hipLaunchKernelGGL((step_front_kernel<false, false, kVecV>), grid, block, lds, s, fp);
+}
+
 hipError_t launch_fused_step(const uint16_t *hidden, const uint16_t *w, float bias,
                              const float *temps, const int32_t *tokens, const uint16_t *logits,
                              int B, int gamma, int d, int V, int mode, const float *cutoff,
@@ -205,36 +340,59 @@ hipError_t launch_fused_step(const uint16_t *hidden, const uint16_t *w, float bi
     if (B > kMaxFusedB) return hipErrorNotSupported;
     char *wsb = static_cast<char *>(ws);
     uint64_t *keys = reinterpret_cast<uint64_t *>(wsb + ws_keys_offset());
+    uint64_t *rkeys = reinterpret_cast<uint64_t *>(wsb + ws_rkeys_offset(B, gamma));
+    uint64_t *rcnt = reinterpret_cast<uint64_t *>(wsb + ws_rcnt_offset());
+    unsigned *arrivals = reinterpret_cast<unsigned *>(wsb + ws_ctrl_offset());
 
+    const int N = B * gamma;
     const bool hvec = (d % 8 == 0) && (((uintptr_t)hidden | (uintptr_t)w) % 16 == 0);
+    const bool ldsw = hvec && d <= kFrontMaxLdsW;
+    const bool select_in_front = mode == DSPARK_CUT_BUDGET && N <= kFusedSelMax;
+    const bool vvec = (V % 8 == 0) && ((uintptr_t)logits % 16 == 0);
     FrontParams fp;
     fp.hidden = hidden;
     fp.w = w;
+    fp.logits = logits;
     fp.temps = temps;
     fp.cutoff = cutoff;
     fp.bias = bias;
+    fp.B = B;
     fp.gamma = gamma;
     fp.d = d;
+    fp.V = V;
     fp.mode = mode;
+    fp.t = (int)(budget < (long long)N ? budget : (long long)N);
     fp.conf = conf;
     fp.surv = surv;
     fp.lengths = lengths;
-    if (hvec && d <= kFrontMaxLdsW)
-        hipLaunchKernelGGL((step_front_kernel<true, true>), dim3(B), dim3(kFrontThreads),
-                           (size_t)d * 2, s, fp);
-    else if (hvec)
-        hipLaunchKernelGGL((step_front_kernel<true, false>), dim3(B), dim3(kFrontThreads), 0, s, fp);
+    fp.rkeys = rkeys;
+    fp.req_arrivals = rcnt;
+    fp.arrivals = select_in_front ? arrivals : nullptr;
+    size_t front_lds = ldsw ? (size_t)d * 2 : 0;
+    if (select_in_front && (size_t)N * 4 > front_lds) front_lds = (size_t)N * 4;
+    // root-row workgroups: a fixed share of the chip, but no more than the
+    // root rows fill with minimum-length sub-chunks
+    const int cus = device_cu_count();
+    const int64_t Vv = vvec ? V / 8 : V;
+    const int64_t root_min_wgs =
+        ((int64_t)B * Vv + kSubMin * (kFrontThreads / kWave) - 1) / (kSubMin * (kFrontThreads / kWave));
+    int64_t root_wgs = (int64_t)kFrontRootWGsPerCU * cus;
+    root_wgs = root_wgs < root_min_wgs ? root_wgs : root_min_wgs;
+    if (root_wgs * (kFrontThreads / kWave) > kMaxWaves) root_wgs = kMaxWaves / (kFrontThreads / kWave);
+    root_wgs = root_wgs < 1 ? 1 : root_wgs;
+    const int root_waves = (int)root_wgs * (kFrontThreads / kWave);
+    if (vvec)
+        launch_front<true>(hvec, ldsw, fp, (int)root_wgs, front_lds, s);
     else
-        hipLaunchKernelGGL((step_front_kernel<false, false>), dim3(B), dim3(kFrontThreads), 0, s, fp);
+        launch_front<false>(hvec, ldsw, fp, (int)root_wgs, front_lds, s);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
 
-    if (mode == DSPARK_CUT_BUDGET) {
+    if (mode == DSPARK_CUT_BUDGET && !select_in_front) {
         e = launch_schedule(surv, B, gamma, mode, cutoff, budget, lengths, s);
         if (e != hipSuccess) return e;
     }
 
-    const bool vvec = (V % 8 == 0) && ((uintptr_t)logits % 16 == 0);
     const size_t lds = (size_t)(2 * B + 1) * sizeof(int);
     StreamParams p;
     p.logits = logits;
@@ -246,19 +404,22 @@ hipError_t launch_fused_step(const uint16_t *hidden, const uint16_t *w, float bi
     p.cu = cu;
     p.ptok = ptok;
     p.psrc = psrc;
+    p.pam = pam;
+    p.acc = acc;
+    p.bonus = bonus;
     p.keys = keys;
-    const dim3 fgrid((B + kFinishThreads / kWave - 1) / (kFinishThreads / kWave));
-    if (vvec) {
-        hipLaunchKernelGGL((step_stream_kernel<true>), dim3(stream_grid<true>(lds)),
-                           dim3(kStreamThreads), lds, s, p);
-        hipLaunchKernelGGL((step_finish_kernel<true>), fgrid, dim3(kFinishThreads), 0, s, keys, cu,
-                           tokens, B, gamma, V, pam, acc, bonus);
-    } else {
-        hipLaunchKernelGGL((step_stream_kernel<false>), dim3(stream_grid<false>(lds)),
-                           dim3(kStreamThreads), lds, s, p);
-        hipLaunchKernelGGL((step_finish_kernel<false>), fgrid, dim3(kFinishThreads), 0, s, keys,
-                           cu, tokens, B, gamma, V, pam, acc, bonus);
-    }
+    p.rkeys = rkeys;
+    p.arrivals = rcnt;
+    p.target_waves = kStreamWavesPerCU * cus < kMaxWaves ? kStreamWavesPerCU * cus : (int)kMaxWaves;
+    p.root_waves = root_waves;
+    // stream grid: enough workgroups for the target waves, at most the resident ones
+    const int stream_wgs_needed = (p.target_waves + kStreamThreads / kWave - 1) / (kStreamThreads / kWave);
+    int g = vvec ? stream_grid<true>(lds) : stream_grid<false>(lds);
+    g = g < stream_wgs_needed ? g : stream_wgs_needed;
+    if (vvec)
+        hipLaunchKernelGGL((step_stream_kernel<true>), dim3(g), dim3(kStreamThreads), lds, s, p);
+    else
+        hipLaunchKernelGGL((step_stream_kernel<false>), dim3(g), dim3(kStreamThreads), lds, s, p);
     return hipGetLastError();
 }
 

@@ -164,8 +164,11 @@ dspark_status dspark_accept(const dspark_bf16 *logits, const int32_t *packed_src
  * with the dense logits [B, gamma+1, V] read only at packed rows.
  * conf and survival may be NULL when the caller does not want them. ws must be
  * zero-filled before its first use with this entry point (dspark_workspace_init
- * does it on a stream); every call leaves it zero-filled again on completion.
- * Calls that share a workspace must not overlap in time.
+ * does it on a stream): its first 256 bytes hold a control word that every
+ * call returns to zero on completion, at the same offset for every size, so
+ * one workspace serves calls of any sizes it is large enough for. The rest is
+ * scratch. Calls that share a workspace must not overlap in time. Batches
+ * above 4096 requests run the same step through the stage kernels.
  */
 dspark_status dspark_step(const dspark_bf16 *hidden, const dspark_bf16 *w, float bias,
                           const float *temps, const int32_t *tokens, const dspark_bf16 *logits,
