@@ -47,9 +47,12 @@ def _load():
         lib.oracle_accept.argtypes = [P, P, P, I, I, P, P]
         lib.oracle_step.argtypes = [P, P, F, P, P, P, I, I, I, ctypes.c_int64, I, P, L,
                                     P, P, P, P, P, P, P, P, P]
+        lib.oracle_cut_static.argtypes = [I, I, P]
+        lib.oracle_cap_accept.argtypes = [P, P, P, I, I, P, P, P]
         for f in (lib.oracle_confidence, lib.oracle_survival, lib.oracle_cut_threshold,
                   lib.oracle_cut_budget, lib.oracle_compact, lib.oracle_argmax_rows,
-                  lib.oracle_accept, lib.oracle_step):
+                  lib.oracle_accept, lib.oracle_step, lib.oracle_cut_static,
+                  lib.oracle_cap_accept):
             f.restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -108,6 +111,37 @@ def cut_budget(surv, budget):
     return L
 
 
+def cut_static(B, gamma):
+    L = np.empty(B, np.int32)
+    _check(_load().oracle_cut_static(int(B), int(gamma), _p(L)), "cut_static")
+    return L
+
+
+def cap_accept(lengths, tokens, amax_full):
+    """Cap-accept verify mode: (accepted, bonus, accepted_full) from the argmax of
+    every row of the full block ([B*(gamma+1)], static packing) and the window
+    lengths."""
+    L = _arr(lengths, np.int32)
+    tok = _arr(tokens, np.int32)
+    B, g1 = tok.shape
+    am = _arr(amax_full, np.int32)
+    assert L.shape == (B,) and am.shape == (B * g1,)
+    acc = np.empty(B, np.int32)
+    bon = np.empty(B, np.int32)
+    full = np.empty(B, np.int32)
+    _check(_load().oracle_cap_accept(_p(L), _p(tok), _p(am), B, g1 - 1, _p(acc), _p(bon),
+                                     _p(full)), "cap_accept")
+    return acc, bon, full
+
+
+def utilization(accepted, accepted_full):
+    """The audit metric: tokens committed under the window over tokens a full
+    verify would have accepted (1.0 when nothing would have been accepted)."""
+    a = int(np.sum(np.asarray(accepted, np.int64)))
+    f = int(np.sum(np.asarray(accepted_full, np.int64)))
+    return 1.0 if f == 0 else a / f
+
+
 def compact(lengths, tokens):
     L = _arr(lengths, np.int32)
     tok = _arr(tokens, np.int32)
@@ -164,7 +198,7 @@ def step(hidden_bits, w_bits, bias, temps, tokens, logits_bits, mode, cutoff=Non
     lg = np.asarray(logits_bits)
     assert lg.dtype == np.uint16 and lg.flags.c_contiguous and lg.shape[:2] == (B, g + 1)
     V = lg.shape[-1]
-    m = {"threshold": 0, "budget": 1}[mode] if isinstance(mode, str) else int(mode)
+    m = {"threshold": 0, "budget": 1, "static": 2}[mode] if isinstance(mode, str) else int(mode)
     c = _arr(cutoff if cutoff is not None else np.zeros(B), np.float32)
     cap = B * (g + 1)
     out = dict(conf=np.empty((B, g)), survival=np.empty((B, g)),

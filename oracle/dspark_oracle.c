@@ -315,9 +315,58 @@ int oracle_accept(const int32_t *cu_seqlens, const int32_t *tokens, const int32_
 }
 
 /*
+ * Step 3 in the static verify mode [P1, "The confidence scheduler and verify
+ * modes"]: the full drafted block is verified, L_b = gamma for every request.
+ * It is the no-trim baseline.
+ */
+int oracle_cut_static(int B, int gamma, int32_t *lengths)
+{
+    if (B < 1 || gamma < 1)
+        return ORACLE_ERR_SHAPE;
+    for (int b = 0; b < B; ++b)
+        lengths[b] = gamma;
+    return ORACLE_OK;
+}
+
+/*
+ * Steps 5b and 6 in the cap-accept verify mode [P1, "The confidence scheduler
+ * and verify modes"]: the block was verified in full (static packing, request
+ * b's rows at b*(gamma+1) + j), but only the scheduled window of L_b drafts may
+ * be committed. The uncapped acceptance records what a full verify gives:
+ *     a_full_b = max m <= gamma with amax[b*(gamma+1) + j] == tokens[b, j+1]
+ *                for all j < m,
+ * the committed count is a_b = min(a_full_b, L_b), and the bonus token is the
+ * target's choice at the first row not committed, bonus_b = amax[b*(gamma+1)
+ * + a_b]. Lengths outside [0, gamma] are rejected.
+ */
+int oracle_cap_accept(const int32_t *lengths, const int32_t *tokens, const int32_t *amax_full,
+                      int B, int gamma, int32_t *accepted, int32_t *bonus,
+                      int32_t *accepted_full)
+{
+    if (B < 1 || gamma < 1)
+        return ORACLE_ERR_SHAPE;
+    for (int b = 0; b < B; ++b) {
+        int32_t L = lengths[b];
+        if (L < 0 || L > gamma)
+            return ORACLE_ERR_RANGE;
+        const int32_t *row_am = amax_full + (size_t)b * (gamma + 1);
+        const int32_t *tok = tokens + (size_t)b * (gamma + 1);
+        int32_t a_full = 0;
+        while (a_full < gamma && row_am[a_full] == tok[a_full + 1])
+            a_full += 1;
+        int32_t a = a_full < L ? a_full : L;
+        accepted_full[b] = a_full;
+        accepted[b] = a;
+        bonus[b] = row_am[a];
+    }
+    return ORACLE_OK;
+}
+
+/*
  * One whole step in the pages' order: confidence -> survival -> cut ->
  * compaction -> argmax over the packed rows only -> acceptance and bonus.
- * mode 0 = per-request cutoffs (cutoff[B]); mode 1 = batch budget (budget).
+ * mode 0 = per-request cutoffs (cutoff[B]); mode 1 = batch budget (budget);
+ * mode 2 = static (the full block).
  * logits is the dense [B, gamma+1, V] block; only packed rows are read.
  * Output buffers: conf/surv [B*gamma]; lengths/accepted/bonus [B];
  * cu_seqlens [B+1]; packed_* [B*(gamma+1)] (entries past cu[B] untouched).
@@ -338,6 +387,8 @@ int oracle_step(const uint16_t *hidden, const uint16_t *w, float bias, const flo
         rc = oracle_cut_threshold(surv, cutoff, B, gamma, lengths);
     else if (mode == 1)
         rc = oracle_cut_budget(surv, B, gamma, budget, lengths);
+    else if (mode == 2)
+        rc = oracle_cut_static(B, gamma, lengths);
     else
         return ORACLE_ERR_ARG;
     if (rc) return rc;

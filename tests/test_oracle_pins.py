@@ -315,6 +315,102 @@ def test_accept_known_planted_prefix(seed):
             assert bon[b] != tok[b, a + 1]
 
 
+# ------------------------------------------------ static and cap-accept modes
+
+def _planted_block(rng, B, g, V):
+    """Dense logits whose every row has a known argmax (+50 in values within
+    [-2, 2]) and drafts agreeing with the rows for exactly m_b positions."""
+    m = rng.integers(0, g + 1, B)
+    top = rng.integers(0, V, (B, g + 1))
+    logits = rng.uniform(-2, 2, (B, g + 1, V)).astype(np.float32)
+    for b in range(B):
+        for j in range(g + 1):
+            logits[b, j, top[b, j]] = 50.0
+    tok = np.zeros((B, g + 1), np.int32)
+    tok[:, 0] = rng.integers(0, V, B)
+    for b in range(B):
+        for j in range(g):
+            tok[b, j + 1] = top[b, j] if j < m[b] else (top[b, j] + 1 + rng.integers(0, V - 1)) % V
+    return bf(logits), tok, top, m
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_cap_accept_known_planted_prefix(seed):
+    # The full block is verified (static packing), the window is L_b: the
+    # uncapped acceptance is the planted agreement m_b, the committed count is
+    # min(L_b, m_b) and the bonus is the known argmax of that row. Catches a
+    # missing cap, capping the record instead of the commit, and a bonus taken
+    # from the wrong row.
+    rng = np.random.default_rng(300 + seed)
+    B, g, V = 7, 6, 257
+    lg, tok, top, m = _planted_block(rng, B, g, V)
+    L = rng.integers(0, g + 1, B).astype(np.int32)
+    am_full = oracle.argmax_rows(lg.reshape(-1, V))
+    acc, bon, full = oracle.cap_accept(L, tok, am_full)
+    for b in range(B):
+        assert full[b] == m[b]
+        a = min(int(L[b]), int(m[b]))
+        assert acc[b] == a and bon[b] == top[b, a]
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_cap_accept_output_equals_compact(seed):
+    # The pages' invariant of the audit arm: cap-accept pays the full verify
+    # but its committed output equals compact's exactly. The two sides take
+    # different routes (argmax of packed rows after compaction, against argmax
+    # of every row then a cap), so an index slip in either shows here.
+    rng = np.random.default_rng(400 + seed)
+    B, g, V = 11, 5, 190
+    lg, tok, top, m = _planted_block(rng, B, g, V)
+    # unplanted noise rows too: overwrite some requests' rows with plain noise
+    noise = bf(rng.standard_normal((B, g + 1, V)))
+    pick = rng.random(B) < 0.4
+    lg = np.where(pick[:, None, None], noise, lg)
+    L = rng.integers(0, g + 1, B).astype(np.int32)
+    cu, pt, ps = oracle.compact(L, tok)
+    am = oracle.argmax_rows(lg.reshape(-1, V), ps[: cu[-1]])
+    acc_c, bon_c = oracle.accept(cu, tok, am)
+    acc, bon, full = oracle.cap_accept(L, tok, oracle.argmax_rows(lg.reshape(-1, V)))
+    assert np.array_equal(acc, acc_c) and np.array_equal(bon, bon_c)
+    assert np.all(full >= acc) and np.all(acc <= L)
+    # where the window is not binding, the record equals the commit
+    loose = full <= L
+    assert np.array_equal(full[loose], acc[loose])
+
+
+def test_static_mode_is_the_full_window():
+    # Static verify: every length is gamma, cu_seqlens is b*(gamma+1), and the
+    # accepted counts are cap-accept's uncapped record. Catches a static mode
+    # that still applies a cut, and a packing that is not the identity.
+    rng = np.random.default_rng(12)
+    B, g, d, V = 5, 4, 32, 150
+    h = bf(rng.standard_normal((B, g, d)))
+    w = bf(rng.standard_normal(d) / math.sqrt(d))
+    temps = (1 + 0.05 * np.arange(g)).astype(np.float32)
+    lg, tok, top, m = _planted_block(rng, B, g, V)
+    o = oracle.step(h, w, 0.0, temps, tok, lg, "static")
+    assert np.all(o["lengths"] == g)
+    assert np.array_equal(o["cu_seqlens"], np.arange(B + 1) * (g + 1))
+    assert np.array_equal(o["packed_src_row"], np.arange(B * (g + 1)))
+    _, _, full = oracle.cap_accept(np.full(B, g, np.int32), tok, o["packed_argmax"])
+    assert np.array_equal(o["accepted"], full) and np.array_equal(full, m)
+    assert np.array_equal(oracle.cut_static(B, g), np.full(B, g))
+
+
+def test_utilization_hand_example():
+    # committed 2 + 0 + 3 = 5 of a full-verify 4 + 1 + 3 = 8: 5/8; a window that
+    # never binds gives 1; nothing acceptable counts as full use.
+    assert oracle.utilization([2, 0, 3], [4, 1, 3]) == 5 / 8
+    assert oracle.utilization([1, 2], [1, 2]) == 1.0
+    assert oracle.utilization([0, 0], [0, 0]) == 1.0
+
+
+def test_cap_accept_rejects_bad_length():
+    with pytest.raises(oracle.OracleError):
+        oracle.cap_accept(np.array([3], np.int32), np.zeros((1, 3), np.int32),
+                          np.zeros(3, np.int32))
+
+
 # --------------------------------------------------------------- whole step
 
 def test_step_equals_stage_chain_and_invariants():
