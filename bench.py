@@ -170,6 +170,40 @@ def run_stage_arm(cfg, slots, outs, ws, steps, dspark, torch):
                 frac_of_hbm_peak=nbytes / (mean_ms / 1e3) / 1e9 / HBM_PEAK_GBS)
 
 
+def run_audit(cfg_t, cfg_b, slots, ws, steps, warmup, dspark, torch):
+    """The static and cap-accept verify modes on the same resident batches: the
+    static step's time (every row of the block verified), the cap-accept
+    kernel's time, and the utilisation of the threshold and budget windows
+    against the full verify (sum committed / sum a full verify accepts)."""
+    dev = slots[0].hidden.device
+    cfg_s = cfg_t.scaled(mode="static")
+    outs_s = [dspark.alloc_step_outputs(cfg_s.B, cfg_s.gamma, dev) for _ in slots]
+    r_s = run_arm(cfg_s, slots, outs_s, ws, steps, warmup, dspark, torch)
+    res = dict(static_full_block=arm_summary(cfg_s, r_s, steps, cfg_s.B))
+    tot = {}
+    cap_ms = []
+    for cfg in (cfg_t, cfg_b):
+        acc_sum = full_sum = 0
+        for i, s in enumerate(slots):
+            o = dspark.dspark_step(s.hidden, s.w, s.bias, s.temps, s.tokens, s.logits, cfg.mode,
+                                   cutoff=s.cutoff, budget=cfg.budget, ws=ws)
+            sums = torch.zeros(2, dtype=torch.int64, device=dev)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            dspark.dspark_cap_accept(outs_s[i]["packed_argmax"], s.tokens, o["lengths"], sums=sums)
+            e1.record()
+            torch.cuda.synchronize()
+            cap_ms.append(e0.elapsed_time(e1))
+            a, f = (int(x) for x in sums.cpu())
+            acc_sum += a
+            full_sum += f
+        tot[cfg.mode] = acc_sum / max(full_sum, 1)
+    res["cap_accept_us"] = 1e3 * sorted(cap_ms)[len(cap_ms) // 2]
+    res["utilization_threshold_window"] = tot["threshold"]
+    res["utilization_budget_window"] = tot["budget"]
+    return res
+
+
 def stream_read_context(torch, dev):
     """HBM GB/s of a plain device-to-device copy of 1 GiB on the same device,
     for context (bytes read plus bytes written over the copy time)."""
@@ -387,6 +421,11 @@ def main():
         r_b = run_arm(cfg_b, slots, outs, ws, args.steps, args.warmup, dspark, torch)
         extra["mixed_budget_T742"] = arm_summary(cfg_b, r_b, args.steps, cfg_b.B)
         log(f"budget arm: {extra['mixed_budget_T742']['rows_per_s']:.3e} rows/s")
+        audit = run_audit(cfg_t, cfg_b, slots, ws, args.steps, args.warmup, dspark, torch)
+        extra["audit_static_cap_accept"] = audit
+        log(f"audit: static {audit['static_full_block']['event_ms_per_step'] * 1e3:.1f} us/step, "
+            f"utilisation thr {audit['utilization_threshold_window']:.3f} "
+            f"bud {audit['utilization_budget_window']:.3f}")
         cfg4 = CONFIGS["budget"]
         p4 = make_params(cfg4)
         slots4 = [make_step(cfg4, i, device=dev, params=p4) for i in range(args.rotation)]

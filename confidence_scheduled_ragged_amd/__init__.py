@@ -21,7 +21,9 @@ LIB_PATH = os.path.join(_HERE, "libdspark.so")
 
 DSPARK_CUT_THRESHOLD = 0
 DSPARK_CUT_BUDGET = 1
-MODES = {"threshold": DSPARK_CUT_THRESHOLD, "budget": DSPARK_CUT_BUDGET}
+DSPARK_CUT_STATIC = 2
+MODES = {"threshold": DSPARK_CUT_THRESHOLD, "budget": DSPARK_CUT_BUDGET,
+         "static": DSPARK_CUT_STATIC}
 
 _lib = None
 
@@ -50,13 +52,14 @@ def lib() -> ctypes.CDLL:
         L.dspark_accept.argtypes = [P, P, P, P, I, I, I, P, P, P, P, S, P]
         L.dspark_step.argtypes = [P, P, F, P, P, P, I, I, I, I, I, P, LL, P, P, P, P, P, P, P, P,
                                   P, P, S, P]
+        L.dspark_cap_accept.argtypes = [P, P, P, I, I, P, P, P, P, P]
         L.dspark_workspace_bytes.argtypes = [I, I, I]
         L.dspark_workspace_bytes.restype = S
         L.dspark_workspace_init.argtypes = [P, S, P]
         L.dspark_status_string.argtypes = [I]
         L.dspark_status_string.restype = ctypes.c_char_p
         for f in (L.dspark_confidence, L.dspark_schedule, L.dspark_compact, L.dspark_accept,
-                  L.dspark_step, L.dspark_workspace_init):
+                  L.dspark_step, L.dspark_workspace_init, L.dspark_cap_accept):
             f.restype = ctypes.c_int
         _lib = L
     return _lib
@@ -237,6 +240,34 @@ STEP_OUTPUTS = ("conf", "survival", "lengths", "cu_seqlens", "packed_tokens", "p
                 "packed_argmax", "accepted", "bonus")
 
 
+def dspark_cap_accept(packed_argmax_full, tokens, lengths, out=None, sums=None):
+    """Cap-accept audit arm over a static verify: (accepted, bonus,
+    accepted_full, sums). packed_argmax_full holds the argmax of every row of
+    the full block (static packing, [B*(gamma+1)]); lengths is the cut's
+    window. sums, when given (int64 [2]), receives (sum accepted, sum
+    accepted_full)."""
+    B, g1 = tokens.shape
+    _need(tokens, "tokens", torch.int32)
+    _need(packed_argmax_full, "packed_argmax_full", torch.int32, (B * g1,))
+    _need(lengths, "lengths", torch.int32, (B,))
+    dev = tokens.device
+    out = out or {}
+    acc = out.get("accepted")
+    bon = out.get("bonus")
+    full = out.get("accepted_full")
+    acc = torch.empty(B, dtype=torch.int32, device=dev) if acc is None else acc
+    bon = torch.empty(B, dtype=torch.int32, device=dev) if bon is None else bon
+    full = torch.empty(B, dtype=torch.int32, device=dev) if full is None else full
+    for t, n in ((acc, "accepted"), (bon, "bonus"), (full, "accepted_full")):
+        _need(t, n, torch.int32, (B,))
+    if sums is not None:
+        _need(sums, "sums", torch.int64, (2,))
+    _ok("dspark_cap_accept", lib().dspark_cap_accept(
+        _ptr(packed_argmax_full), _ptr(tokens), _ptr(lengths), B, g1 - 1, _ptr(acc), _ptr(bon),
+        _ptr(full), _ptr(sums), _stream(dev)))
+    return acc, bon, full, sums
+
+
 def alloc_step_outputs(B: int, gamma: int, device, with_conf: bool = True) -> Dict[str, torch.Tensor]:
     cap = B * (gamma + 1)
     i32 = dict(dtype=torch.int32, device=device)
@@ -284,6 +315,7 @@ def dspark_step(hidden, w, bias, temps, tokens, logits, mode, cutoff=None, budge
 
 
 __all__ = ["DsparkError", "lib", "LIB_PATH", "dspark_status_string", "dspark_confidence", "dspark_schedule",
-           "dspark_compact", "dspark_accept", "dspark_step", "dspark_workspace_bytes",
+           "dspark_compact", "dspark_accept", "dspark_step", "dspark_cap_accept",
+           "dspark_workspace_bytes",
            "dspark_workspace_init", "workspace", "alloc_step_outputs", "STEP_OUTPUTS",
-           "DSPARK_CUT_THRESHOLD", "DSPARK_CUT_BUDGET"]
+           "DSPARK_CUT_THRESHOLD", "DSPARK_CUT_BUDGET", "DSPARK_CUT_STATIC"]

@@ -57,6 +57,10 @@ inline dspark_status check_bg(int B, int gamma) {
     return DSPARK_OK;
 }
 
+inline bool valid_mode(int mode) {
+    return mode == DSPARK_CUT_THRESHOLD || mode == DSPARK_CUT_BUDGET || mode == DSPARK_CUT_STATIC;
+}
+
 inline dspark_status launched(hipError_t e) { return e == hipSuccess ? DSPARK_OK : DSPARK_ERR_HIP; }
 
 inline hipStream_t as_stream(void *s) { return static_cast<hipStream_t>(s); }
@@ -107,7 +111,7 @@ DSPARK_API dspark_status dspark_schedule(const float *survival, int B, int gamma
     if (!survival || !lengths) return DSPARK_ERR_NULL;
     if (mode == DSPARK_CUT_THRESHOLD && !cutoff) return DSPARK_ERR_NULL;
     if (dspark_status st = check_bg(B, gamma)) return st;
-    if (mode != DSPARK_CUT_THRESHOLD && mode != DSPARK_CUT_BUDGET) return DSPARK_ERR_ARG;
+    if (!valid_mode(mode)) return DSPARK_ERR_ARG;
     if (mode == DSPARK_CUT_BUDGET && budget < 0) return DSPARK_ERR_ARG;
     if (misaligned(survival, 4) || misaligned(cutoff, 4) || misaligned(lengths, 4))
         return DSPARK_ERR_ALIGN;
@@ -153,6 +157,22 @@ DSPARK_API dspark_status dspark_accept(const dspark_bf16 *logits, const int32_t 
                                   packed_argmax, accepted, bonus, ws, as_stream(stream)));
 }
 
+DSPARK_API dspark_status dspark_cap_accept(const int32_t *packed_argmax_full,
+                                           const int32_t *tokens, const int32_t *lengths, int B,
+                                           int gamma, int32_t *accepted, int32_t *bonus,
+                                           int32_t *accepted_full, long long *sums,
+                                           void *stream) {
+    if (!packed_argmax_full || !tokens || !lengths || !accepted || !bonus || !accepted_full)
+        return DSPARK_ERR_NULL;
+    if (dspark_status st = check_bg(B, gamma)) return st;
+    if (misaligned(packed_argmax_full, 4) || misaligned(tokens, 4) || misaligned(lengths, 4) ||
+        misaligned(accepted, 4) || misaligned(bonus, 4) || misaligned(accepted_full, 4) ||
+        misaligned(sums, 8))
+        return DSPARK_ERR_ALIGN;
+    return launched(launch_cap_accept(packed_argmax_full, tokens, lengths, B, gamma, accepted,
+                                      bonus, accepted_full, sums, as_stream(stream)));
+}
+
 DSPARK_API dspark_status dspark_step(const dspark_bf16 *hidden, const dspark_bf16 *w, float bias,
                                      const float *temps, const int32_t *tokens,
                                      const dspark_bf16 *logits, int B, int gamma, int d, int V,
@@ -167,7 +187,7 @@ DSPARK_API dspark_status dspark_step(const dspark_bf16 *hidden, const dspark_bf1
     if (mode == DSPARK_CUT_THRESHOLD && !cutoff) return DSPARK_ERR_NULL;
     if (dspark_status st = check_bg(B, gamma)) return st;
     if (d < 1 || d > kMaxD || V < 1) return DSPARK_ERR_SHAPE;
-    if (mode != DSPARK_CUT_THRESHOLD && mode != DSPARK_CUT_BUDGET) return DSPARK_ERR_ARG;
+    if (!valid_mode(mode)) return DSPARK_ERR_ARG;
     if (mode == DSPARK_CUT_BUDGET && budget < 0) return DSPARK_ERR_ARG;
     if (!std::isfinite(bias)) return DSPARK_ERR_ARG;
     if (misaligned(hidden, 2) || misaligned(w, 2) || misaligned(temps, 4) ||

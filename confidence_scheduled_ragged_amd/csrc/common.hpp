@@ -142,6 +142,9 @@ hipError_t launch_fill_zero(void *ws, size_t bytes, hipStream_t s);
 // The fused step in two launches. Returns hipErrorNotSupported (enqueuing
 // nothing) when the sizes are outside what it handles; the caller then runs
 // the stage kernels instead.
+hipError_t launch_cap_accept(const int32_t *pam_full, const int32_t *tokens,
+                             const int32_t *lengths, int B, int gamma, int32_t *acc,
+                             int32_t *bonus, int32_t *acc_full, long long *sums, hipStream_t s);
 hipError_t launch_fused_step(const uint16_t *hidden, const uint16_t *w, float bias,
                              const float *temps, const int32_t *tokens, const uint16_t *logits,
                              int B, int gamma, int d, int V, int mode, const float *cutoff,

@@ -133,6 +133,10 @@ __global__ __launch_bounds__(kFrontThreads) void step_front_kernel(FrontParams p
         if (tid == 0) p.lengths[b] = threshold_length(s_s, p.gamma, p.cutoff[b]);
         return;
     }
+    if (p.mode == DSPARK_CUT_STATIC) {
+        if (tid == 0) p.lengths[b] = p.gamma;
+        return;
+    }
     if (!select_here) return;
 
     // budget: count this request as done once its survival stores are complete;

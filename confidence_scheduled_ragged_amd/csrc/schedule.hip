@@ -30,12 +30,21 @@ __global__ __launch_bounds__(kBudgetThreads) void schedule_budget_kernel(
     budget_lengths(surv, B, gamma, cut, lengths, scan_lds);
 }
 
+__global__ __launch_bounds__(kThreshThreads) void schedule_static_kernel(int B, int gamma,
+                                                                      int32_t *__restrict__ lengths) {
+    const int b = blockIdx.x * blockDim.x + threadIdx.x;
+    if (b < B) lengths[b] = gamma;
+}
+
 hipError_t launch_schedule(const float *surv, int B, int gamma, int mode, const float *cutoff,
                            long long budget, int32_t *lengths, hipStream_t s) {
     if (mode == DSPARK_CUT_THRESHOLD) {
         dim3 grid((B + kThreshThreads - 1) / kThreshThreads), block(kThreshThreads);
         hipLaunchKernelGGL(schedule_threshold_kernel, grid, block, 0, s, surv, cutoff, B, gamma,
                            lengths);
+    } else if (mode == DSPARK_CUT_STATIC) {
+        dim3 grid((B + kThreshThreads - 1) / kThreshThreads), block(kThreshThreads);
+        hipLaunchKernelGGL(schedule_static_kernel, grid, block, 0, s, B, gamma, lengths);
     } else {
         hipLaunchKernelGGL(schedule_budget_kernel, dim3(1), dim3(kBudgetThreads), 0, s, surv, B,
                            gamma, budget, lengths);

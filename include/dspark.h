@@ -10,7 +10,11 @@
  *   4. ragged compaction into a packed verify batch     (dspark_compact)
  *   5. greedy acceptance against the target's argmax    (dspark_accept)
  *   6. bonus token                                      (dspark_accept)
- * or all six in one call (dspark_step).
+ * or all six in one call (dspark_step). The verify modes of [P1, "The
+ * confidence scheduler and verify modes"]: compact (the cut window, the
+ * production path), static (DSPARK_CUT_STATIC, the full block) and cap-accept
+ * (dspark_cap_accept over a static verify: commits the window, records the
+ * full-verify acceptance for the utilisation audit).
  *
  * Sources (web pages): [P1] "DFlash to DSpark in SGLang: 4.3x faster decode,
  * and DeepSeek-V4 support" (yichizhang.dev tutorial); [P2] SGLang's DSpark
@@ -76,7 +80,8 @@ typedef enum dspark_status {
 
 typedef enum dspark_cut_mode {
     DSPARK_CUT_THRESHOLD = 0, /* per-request marginal cost cutoff[b] */
-    DSPARK_CUT_BUDGET = 1     /* batch-wide budget of `budget` drafted positions */
+    DSPARK_CUT_BUDGET = 1,    /* batch-wide budget of `budget` drafted positions */
+    DSPARK_CUT_STATIC = 2     /* the full block: L_b = gamma (no-trim baseline) */
 } dspark_cut_mode;
 
 #define DSPARK_MAX_GAMMA 256
@@ -111,6 +116,9 @@ dspark_status dspark_confidence(const dspark_bf16 *hidden, const dspark_bf16 *w,
  *     descending, ties by lower request then lower position, and keep the
  *     first min(budget, B*gamma); L_b counts request b's kept pairs. `cutoff`
  *     is ignored and may be NULL; budget >= 0.
+ *   DSPARK_CUT_STATIC [P1, "The confidence scheduler and verify modes"]: the
+ *     static verify mode, L_b = gamma for every request; survival is not read,
+ *     `cutoff` and `budget` are ignored.
  * survival [B, gamma] fp32 (finite); lengths [B] int32 output.
  */
 dspark_status dspark_schedule(const float *survival, int B, int gamma, int mode,
@@ -158,10 +166,35 @@ dspark_status dspark_accept(const dspark_bf16 *logits, const int32_t *packed_src
                             void *ws, size_t ws_bytes, void *stream);
 
 /*
+ * Steps 5b-6 in the cap-accept verify mode [P1, "The confidence scheduler and
+ * verify modes"]: the audit arm pays the full (static) verify but commits only
+ * the scheduled window, so its committed output equals the compact mode's
+ * exactly while it records what a full verify would have accepted.
+ *   packed_argmax_full [B*(gamma+1)] int32: the target's choice at every row
+ *     of the full block, static packing (request b's row j at b*(gamma+1)+j),
+ *     e.g. the packed_argmax of dspark_step in DSPARK_CUT_STATIC mode;
+ *   tokens [B, gamma+1] int32; lengths [B] int32: the window L_b of the cut
+ *     (clamped to [0, gamma]).
+ *   accepted_full[b] = largest m <= gamma with
+ *                      packed_argmax_full[b*(gamma+1)+j] == tokens[b,j+1], j < m
+ *   accepted[b]      = min(accepted_full[b], L_b)
+ *   bonus[b]         = packed_argmax_full[b*(gamma+1) + accepted[b]]
+ *   sums (nullable) [2] int64: sum of accepted, sum of accepted_full; their
+ *     ratio is the utilisation of the window against the full verify.
+ * All outputs are device int32 [B] (sums int64 [2]).
+ */
+dspark_status dspark_cap_accept(const int32_t *packed_argmax_full, const int32_t *tokens,
+                                const int32_t *lengths, int B, int gamma, int32_t *accepted,
+                                int32_t *bonus, int32_t *accepted_full, long long *sums,
+                                void *stream);
+
+/*
  * Steps 1-6 fused, the production "compact" verify mode of [P1, "The
  * confidence scheduler and verify modes"]: the result equals dspark_confidence
  * -> dspark_schedule -> dspark_compact -> dspark_accept on the same inputs,
- * with the dense logits [B, gamma+1, V] read only at packed rows.
+ * with the dense logits [B, gamma+1, V] read only at packed rows. With
+ * DSPARK_CUT_STATIC it is the static mode (every row verified; its
+ * packed_argmax and accepted feed dspark_cap_accept for the audit arm).
  * conf and survival may be NULL when the caller does not want them. ws must be
  * zero-filled before its first use with this entry point (dspark_workspace_init
  * does it on a stream): its first 256 bytes hold a control word that every

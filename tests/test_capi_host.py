@@ -92,7 +92,8 @@ def test_schedule_validation(L):
     assert sched_call(L, lengths=0) == ENULL
     assert sched_call(L, cutoff=0, mode=0) == ENULL
     assert sched_call(L, B=-1) == ESHAPE
-    assert sched_call(L, mode=2, cutoff=0) == EARG
+    assert sched_call(L, mode=3, cutoff=0) == EARG
+    assert sched_call(L, mode=-1, cutoff=0) == EARG
     assert sched_call(L, mode=1, cutoff=0, budget=-1) == EARG
     assert sched_call(L, lengths=A + 1) == EALIGN
     assert sched_call(L, mode=1, cutoff=0, surv=A + 2) == EALIGN
@@ -157,6 +158,23 @@ def test_step_validation(L):
     assert step_call(L, tokens=A + 2) == EALIGN
     assert step_call(L, ws=A + 4) == EALIGN
     assert step_call(L, wsb=100) == EWS
+
+
+def cap_call(L, pam=A, tok=A, lengths=A, B=4, g=8, acc=A, bon=A, full=A, sums=0):
+    f = lambda x: P(x) if x else None
+    return L.dspark_cap_accept(f(pam), f(tok), f(lengths), B, g, f(acc), f(bon), f(full),
+                               f(sums), None)
+
+
+def test_cap_accept_validation(L):
+    assert cap_call(L, pam=0) == ENULL
+    assert cap_call(L, full=0) == ENULL
+    assert cap_call(L, B=0) == ESHAPE
+    assert cap_call(L, g=0) == ESHAPE
+    assert cap_call(L, g=300) == ESHAPE
+    assert cap_call(L, acc=A + 2) == EALIGN
+    assert cap_call(L, B=-3, sums=A + 4) == ESHAPE     # shape is checked before alignment
+    assert cap_call(L, sums=A + 4) == EALIGN
 
 
 def test_workspace_init_validation(L):
