@@ -204,6 +204,40 @@ def run_audit(cfg_t, cfg_b, slots, ws, steps, warmup, dspark, torch):
     return res
 
 
+def run_gather(cfg, outs, steps, dspark, torch, width=7168):
+    """The packed activation gather: per-position bf16 activations
+    [B*(gamma+1), width] of the target moved to [total, width] through the
+    packed source rows of the fused threshold steps. One distinct activation
+    tensor per resident batch, so rows are not re-read from the Infinity Cache.
+    Bytes: every packed row read once and written once."""
+    dev = outs[0]["cu_seqlens"].device
+    cap = cfg.B * (cfg.gamma + 1)
+    R = len(outs)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(0)
+    acts = [torch.randn((cap, width), generator=gen, device=dev).to(torch.bfloat16)
+            for _ in range(R)]
+    dst = torch.empty((cap, width), dtype=torch.bfloat16, device=dev)
+    totals = [int(o["cu_seqlens"][-1].item()) for o in outs]
+    for i in range(R):
+        dspark.dspark_gather_rows(acts[i], outs[i]["packed_src_row"], outs[i]["cu_seqlens"],
+                                  out=dst)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(steps):
+        dspark.dspark_gather_rows(acts[i % R], outs[i % R]["packed_src_row"],
+                                  outs[i % R]["cu_seqlens"], out=dst)
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / steps
+    nbytes = sum(2 * totals[i % R] * width * 2 for i in range(steps)) / steps
+    del acts, dst
+    return dict(width=width, dtype="bf16", us_per_call=us, mean_packed_rows=sum(totals) / R,
+                bytes_per_call=nbytes, achieved_gbs=nbytes / (us / 1e6) / 1e9,
+                frac_of_hbm_peak=nbytes / (us / 1e6) / 1e9 / HBM_PEAK_GBS)
+
+
 def stream_read_context(torch, dev):
     """HBM GB/s of a plain device-to-device copy of 1 GiB on the same device,
     for context (bytes read plus bytes written over the copy time)."""
@@ -417,6 +451,10 @@ def main():
         extra["stages_a3_a6_threshold"] = st
         log(f"stage path a3-a6: {st['event_ms_per_step'] * 1e3:.1f} us/step, "
             f"{st['achieved_gbs']:.0f} GB/s")
+        ga = run_gather(cfg_t, outs, args.steps, dspark, torch)
+        extra["packed_activation_gather_7168"] = ga
+        log(f"packed activation gather (7168 bf16): {ga['us_per_call']:.1f} us, "
+            f"{ga['achieved_gbs']:.0f} GB/s")
         # budget arm on the same resident batches (the two arms share their seeds)
         r_b = run_arm(cfg_b, slots, outs, ws, args.steps, args.warmup, dspark, torch)
         extra["mixed_budget_T742"] = arm_summary(cfg_b, r_b, args.steps, cfg_b.B)

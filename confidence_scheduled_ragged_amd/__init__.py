@@ -53,13 +53,15 @@ def lib() -> ctypes.CDLL:
         L.dspark_step.argtypes = [P, P, F, P, P, P, I, I, I, I, I, P, LL, P, P, P, P, P, P, P, P,
                                   P, P, S, P]
         L.dspark_cap_accept.argtypes = [P, P, P, I, I, P, P, P, P, P]
+        L.dspark_gather_rows.argtypes = [P, P, P, I, I, LL, P, P]
         L.dspark_workspace_bytes.argtypes = [I, I, I]
         L.dspark_workspace_bytes.restype = S
         L.dspark_workspace_init.argtypes = [P, S, P]
         L.dspark_status_string.argtypes = [I]
         L.dspark_status_string.restype = ctypes.c_char_p
         for f in (L.dspark_confidence, L.dspark_schedule, L.dspark_compact, L.dspark_accept,
-                  L.dspark_step, L.dspark_workspace_init, L.dspark_cap_accept):
+                  L.dspark_step, L.dspark_workspace_init, L.dspark_cap_accept,
+                  L.dspark_gather_rows):
             f.restype = ctypes.c_int
         _lib = L
     return _lib
@@ -240,6 +242,39 @@ STEP_OUTPUTS = ("conf", "survival", "lengths", "cu_seqlens", "packed_tokens", "p
                 "packed_argmax", "accepted", "bonus")
 
 
+def dspark_gather_rows(src, packed_src_row, cu_seqlens, out=None):
+    """Packed row gather: out[r] = src[packed_src_row[r]] for r < cu_seqlens[B].
+    src is [B*(gamma+1), ...] (or [B, gamma+1, ...]) of any dtype; out has the
+    same row shape and B*(gamma+1) rows (allocated when None)."""
+    _need(cu_seqlens, "cu_seqlens", torch.int32)
+    B = cu_seqlens.numel() - 1
+    _need(packed_src_row, "packed_src_row", torch.int32)
+    cap = packed_src_row.numel()
+    if cap % B != 0:
+        raise ValueError("packed_src_row must have B*(gamma+1) entries")
+    g = cap // B - 1
+    if not isinstance(src, torch.Tensor) or src.device.type != "cuda" or not src.is_contiguous():
+        raise ValueError("src must be a contiguous GPU tensor")
+    if src.numel() % cap != 0:
+        raise ValueError("src must hold B*(gamma+1) rows")
+    if src.shape[0] == cap:
+        row_shape = (cap,) + tuple(src.shape[1:])
+    elif src.dim() >= 2 and tuple(src.shape[:2]) == (B, g + 1):
+        row_shape = (cap,) + tuple(src.shape[2:])
+    else:
+        raise ValueError("src must be [B*(gamma+1), ...] or [B, gamma+1, ...]")
+    row_bytes = src.numel() // cap * src.element_size()
+    if out is None:
+        out = torch.empty(row_shape, dtype=src.dtype, device=src.device)
+    if (out.dtype != src.dtype or not out.is_contiguous() or out.device != src.device
+            or out.numel() * out.element_size() != cap * row_bytes):
+        raise ValueError("out must be a contiguous GPU tensor of B*(gamma+1) rows like src")
+    _ok("dspark_gather_rows", lib().dspark_gather_rows(
+        _ptr(src), _ptr(packed_src_row), _ptr(cu_seqlens), B, g, row_bytes, _ptr(out),
+        _stream(src.device)))
+    return out
+
+
 def dspark_cap_accept(packed_argmax_full, tokens, lengths, out=None, sums=None):
     """Cap-accept audit arm over a static verify: (accepted, bonus,
     accepted_full, sums). packed_argmax_full holds the argmax of every row of
@@ -316,6 +351,7 @@ def dspark_step(hidden, w, bias, temps, tokens, logits, mode, cutoff=None, budge
 
 __all__ = ["DsparkError", "lib", "LIB_PATH", "dspark_status_string", "dspark_confidence", "dspark_schedule",
            "dspark_compact", "dspark_accept", "dspark_step", "dspark_cap_accept",
+           "dspark_gather_rows",
            "dspark_workspace_bytes",
            "dspark_workspace_init", "workspace", "alloc_step_outputs", "STEP_OUTPUTS",
            "DSPARK_CUT_THRESHOLD", "DSPARK_CUT_BUDGET", "DSPARK_CUT_STATIC"]

@@ -136,8 +136,20 @@ DSPARK_API dspark_status dspark_compact(const int32_t *lengths, const int32_t *t
     hipError_t e = launch_compact(lengths, tokens, B, gamma, cu_seqlens, packed_tokens,
                                   packed_src_row, s);
     if (e == hipSuccess && logits)
-        e = launch_gather_rows(logits, packed_src_row, cu_seqlens, B, gamma, V, packed_logits, s);
+        e = launch_gather_rows(logits, packed_src_row, cu_seqlens, B, gamma, (int64_t)V * 2,
+                               packed_logits, s);
     return launched(e);
+}
+
+DSPARK_API dspark_status dspark_gather_rows(const void *src, const int32_t *packed_src_row,
+                                            const int32_t *cu_seqlens, int B, int gamma,
+                                            long long row_bytes, void *dst, void *stream) {
+    if (!src || !packed_src_row || !cu_seqlens || !dst) return DSPARK_ERR_NULL;
+    if (dspark_status st = check_bg(B, gamma)) return st;
+    if (row_bytes < 1 || row_bytes > ((long long)1 << 40)) return DSPARK_ERR_SHAPE;
+    if (misaligned(packed_src_row, 4) || misaligned(cu_seqlens, 4)) return DSPARK_ERR_ALIGN;
+    return launched(launch_gather_rows(src, packed_src_row, cu_seqlens, B, gamma,
+                                       (int64_t)row_bytes, dst, as_stream(stream)));
 }
 
 DSPARK_API dspark_status dspark_accept(const dspark_bf16 *logits, const int32_t *packed_src_row,

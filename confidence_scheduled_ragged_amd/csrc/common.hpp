@@ -132,8 +132,8 @@ hipError_t launch_schedule(const float *surv, int B, int gamma, int mode, const 
                            long long budget, int32_t *lengths, hipStream_t s);
 hipError_t launch_compact(const int32_t *lengths, const int32_t *tokens, int B, int gamma,
                           int32_t *cu, int32_t *ptok, int32_t *psrc, hipStream_t s);
-hipError_t launch_gather_rows(const uint16_t *logits, const int32_t *psrc, const int32_t *cu,
-                              int B, int gamma, int V, uint16_t *out, hipStream_t s);
+hipError_t launch_gather_rows(const void *src, const int32_t *psrc, const int32_t *cu, int B,
+                              int gamma, int64_t row_bytes, void *dst, hipStream_t s);
 hipError_t launch_accept(const uint16_t *logits, const int32_t *psrc, const int32_t *cu,
                          const int32_t *tokens, int B, int gamma, int V, int32_t *pam,
                          int32_t *acc, int32_t *bonus, void *ws, hipStream_t s);

@@ -51,36 +51,53 @@ __global__ __launch_bounds__(kCompactThreads) void compact_kernel(
     }
 }
 
-// Optional row gather: packed_logits[r, :] = logits[psrc[r], :] for r < cu[B].
-// blockIdx.y strides over packed rows, blockIdx.x * blockDim over 16-byte
-// slots of a row (or 2-byte elements when rows are not 16-byte aligned).
-template <bool kVec>
-__global__ __launch_bounds__(256) void gather_rows_kernel(const uint16_t *__restrict__ logits,
+// Row gather through the packed source rows: dst[r, :] = src[psrc[r], :] for
+// r < cu[B], rows of `row_elems` elements of type T (16, 4 or 1 bytes).
+// blockIdx.y strides over packed rows, blockIdx.x * blockDim over a row's
+// elements; each thread has four loads in flight before it stores. A source
+// row outside [0, cap) leaves its packed row untouched.
+template <typename T>
+__global__ __launch_bounds__(256) void gather_rows_kernel(const T *__restrict__ src,
                                                           const int32_t *__restrict__ psrc,
                                                           const int32_t *__restrict__ cu, int B,
-                                                          int gamma, int V,
-                                                          uint16_t *__restrict__ out) {
-    const int cap = B * (gamma + 1);
+                                                          int cap, int64_t row_elems,
+                                                          T *__restrict__ dst) {
+    constexpr int kUnroll = 4;
     int total = cu[B];
     total = total < 0 ? 0 : (total > cap ? cap : total);
-    const int64_t slots = kVec ? (V >> 3) : V;
+    const int64_t step = (int64_t)gridDim.x * blockDim.x * kUnroll;
     for (int r = blockIdx.y; r < total; r += gridDim.y) {
-        const int src = psrc[r];
-        if (src < 0 || src >= cap) continue;
-        if (kVec) {
-            const u32x4 *in4 = reinterpret_cast<const u32x4 *>(logits + (size_t)src * V);
-            u32x4 *o4 = reinterpret_cast<u32x4 *>(out + (size_t)r * V);
-            for (int64_t v = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; v < slots;
-                 v += (int64_t)gridDim.x * blockDim.x)
-                __builtin_nontemporal_store(__builtin_nontemporal_load(in4 + v), o4 + v);
-        } else {
-            const uint16_t *in = logits + (size_t)src * V;
-            uint16_t *o = out + (size_t)r * V;
-            for (int64_t v = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; v < slots;
-                 v += (int64_t)gridDim.x * blockDim.x)
-                o[v] = in[v];
+        const int s = psrc[r];
+        if (s < 0 || s >= cap) continue;
+        const T *in = src + (size_t)s * (size_t)row_elems;
+        T *out = dst + (size_t)r * (size_t)row_elems;
+        for (int64_t c0 = (int64_t)blockIdx.x * blockDim.x * kUnroll + threadIdx.x; c0 < row_elems;
+             c0 += step) {
+            T v[kUnroll];
+#pragma unroll
+            for (int u = 0; u < kUnroll; ++u) {
+                const int64_t c = c0 + (int64_t)u * blockDim.x;
+                if (c < row_elems) v[u] = __builtin_nontemporal_load(in + c);
+            }
+#pragma unroll
+            for (int u = 0; u < kUnroll; ++u) {
+                const int64_t c = c0 + (int64_t)u * blockDim.x;
+                if (c < row_elems) __builtin_nontemporal_store(v[u], out + c);
+            }
         }
     }
+}
+
+template <typename T>
+static void launch_gather_typed(const void *src, const int32_t *psrc, const int32_t *cu, int B,
+                                int gamma, int64_t row_elems, void *dst, hipStream_t s) {
+    const int cap = B * (gamma + 1);
+    int64_t gx = (row_elems + 256 * 4 - 1) / (256 * 4);
+    gx = gx < 1 ? 1 : (gx > 64 ? 64 : gx);
+    const int gy = cap < 4096 ? cap : 4096;
+    hipLaunchKernelGGL((gather_rows_kernel<T>), dim3((unsigned)gx, gy), dim3(256), 0, s,
+                       static_cast<const T *>(src), psrc, cu, B, cap, row_elems,
+                       static_cast<T *>(dst));
 }
 
 hipError_t launch_compact(const int32_t *lengths, const int32_t *tokens, int B, int gamma,
@@ -90,20 +107,15 @@ hipError_t launch_compact(const int32_t *lengths, const int32_t *tokens, int B, 
     return hipGetLastError();
 }
 
-hipError_t launch_gather_rows(const uint16_t *logits, const int32_t *psrc, const int32_t *cu,
-                              int B, int gamma, int V, uint16_t *out, hipStream_t s) {
-    const bool vec = (V % 8 == 0) && (((uintptr_t)logits | (uintptr_t)out) % 16 == 0);
-    const int64_t slots = vec ? V / 8 : V;
-    const int cap = B * (gamma + 1);
-    int gx = (int)((slots + 256 * 4 - 1) / (256 * 4));
-    gx = gx < 1 ? 1 : (gx > 64 ? 64 : gx);
-    int gy = cap < 4096 ? cap : 4096;
-    if (vec)
-        hipLaunchKernelGGL((gather_rows_kernel<true>), dim3(gx, gy), dim3(256), 0, s, logits, psrc,
-                           cu, B, gamma, V, out);
+hipError_t launch_gather_rows(const void *src, const int32_t *psrc, const int32_t *cu, int B,
+                              int gamma, int64_t row_bytes, void *dst, hipStream_t s) {
+    const uintptr_t al = (uintptr_t)src | (uintptr_t)dst;
+    if (row_bytes % 16 == 0 && al % 16 == 0)
+        launch_gather_typed<u32x4>(src, psrc, cu, B, gamma, row_bytes / 16, dst, s);
+    else if (row_bytes % 4 == 0 && al % 4 == 0)
+        launch_gather_typed<uint32_t>(src, psrc, cu, B, gamma, row_bytes / 4, dst, s);
     else
-        hipLaunchKernelGGL((gather_rows_kernel<false>), dim3(gx, gy), dim3(256), 0, s, logits,
-                           psrc, cu, B, gamma, V, out);
+        launch_gather_typed<uint8_t>(src, psrc, cu, B, gamma, row_bytes, dst, s);
     return hipGetLastError();
 }
 

@@ -7,7 +7,8 @@
  *   1. confidence head with per-position temperature  (dspark_confidence)
  *   2. survival curve, the running product of scores   (dspark_confidence)
  *   3. verify-length cut, per request or batch budget   (dspark_schedule)
- *   4. ragged compaction into a packed verify batch     (dspark_compact)
+ *   4. ragged compaction into a packed verify batch     (dspark_compact,
+ *      and dspark_gather_rows for per-position activations)
  *   5. greedy acceptance against the target's argmax    (dspark_accept)
  *   6. bonus token                                      (dspark_accept)
  * or all six in one call (dspark_step). The verify modes of [P1, "The
@@ -142,6 +143,22 @@ dspark_status dspark_compact(const int32_t *lengths, const int32_t *tokens, int 
                              int32_t *cu_seqlens, int32_t *packed_tokens,
                              int32_t *packed_src_row, const dspark_bf16 *logits, int V,
                              dspark_bf16 *packed_logits, void *stream);
+
+/*
+ * Packed row gather [P1, "Ragged verify under full CUDA graphs"]: the
+ * scheduled verify tokens are front-packed into one [total_tokens, hidden]
+ * buffer, the layout the target's per-row matmuls already use. Gathers rows of
+ * any width through the packed source rows of dspark_compact:
+ *   dst[r, :] = src[packed_src_row[r], :]   for r < cu_seqlens[B]
+ * src: B*(gamma+1) rows of row_bytes bytes (e.g. per-position activations
+ * [B, gamma+1, hidden]); dst: capacity B*(gamma+1) rows of row_bytes. Rows at
+ * and past cu_seqlens[B], and rows whose source index lies outside
+ * [0, B*(gamma+1)), are left untouched. 16-byte accesses are used when
+ * row_bytes and both pointers allow it, 4-byte or 1-byte otherwise.
+ */
+dspark_status dspark_gather_rows(const void *src, const int32_t *packed_src_row,
+                                 const int32_t *cu_seqlens, int B, int gamma, long long row_bytes,
+                                 void *dst, void *stream);
 
 /*
  * Steps 5-6 [P1, "Background"]: greedy verification commits the longest

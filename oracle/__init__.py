@@ -49,10 +49,11 @@ def _load():
                                     P, P, P, P, P, P, P, P, P]
         lib.oracle_cut_static.argtypes = [I, I, P]
         lib.oracle_cap_accept.argtypes = [P, P, P, I, I, P, P, P]
+        lib.oracle_gather_rows.argtypes = [P, P, P, I, I, ctypes.c_int64, P]
         for f in (lib.oracle_confidence, lib.oracle_survival, lib.oracle_cut_threshold,
                   lib.oracle_cut_budget, lib.oracle_compact, lib.oracle_argmax_rows,
                   lib.oracle_accept, lib.oracle_step, lib.oracle_cut_static,
-                  lib.oracle_cap_accept):
+                  lib.oracle_cap_accept, lib.oracle_gather_rows):
             f.restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -156,6 +157,24 @@ def compact(lengths, tokens):
                                   ctypes.cast(ctypes.pointer(total), ctypes.c_void_p)),
            "compact")
     return cu, ptok, psrc
+
+
+def gather_rows(src, packed_src_row, cu_seqlens, dst=None):
+    """Packed row gather of a [B*(gamma+1), ...] array of any dtype: row r <
+    cu[B] of the result is row packed_src_row[r] of src; the rest of dst (a
+    copy of the given one, or zeros) is left as it is."""
+    a = np.ascontiguousarray(src)
+    cu = _arr(cu_seqlens, np.int32)
+    ps = _arr(packed_src_row, np.int32)
+    B = cu.shape[0] - 1
+    cap = ps.shape[0]
+    g = cap // B - 1
+    assert cap == B * (g + 1) and a.shape[0] == cap
+    out = np.zeros_like(a) if dst is None else np.array(dst, dtype=a.dtype, copy=True)
+    row_bytes = a.nbytes // cap
+    _check(_load().oracle_gather_rows(_p(a), _p(ps), _p(cu), B, g, row_bytes, _p(out)),
+           "gather_rows")
+    return out
 
 
 def argmax_rows(logits_bits, src_rows=None):

@@ -250,6 +250,33 @@ int oracle_compact(const int32_t *lengths, const int32_t *tokens, int B, int gam
 }
 
 /*
+ * Packed row gather [P1, "Ragged verify under full CUDA graphs"]: the
+ * scheduled verify tokens' per-row data is front-packed into one
+ * [total_tokens, hidden] buffer. Row r < cu[B] of dst is a byte copy of row
+ * packed_src_row[r] of src (rows of row_bytes bytes); later rows are left as
+ * they are. A source row outside [0, B*(gamma+1)) is rejected.
+ */
+int oracle_gather_rows(const uint8_t *src, const int32_t *packed_src_row,
+                       const int32_t *cu_seqlens, int B, int gamma, int64_t row_bytes,
+                       uint8_t *dst)
+{
+    if (B < 1 || gamma < 1 || row_bytes < 1)
+        return ORACLE_ERR_SHAPE;
+    int64_t cap = (int64_t)B * (gamma + 1);
+    int64_t total = cu_seqlens[B];
+    if (total < 0 || total > cap)
+        return ORACLE_ERR_RANGE;
+    for (int64_t r = 0; r < total; ++r) {
+        int64_t s = packed_src_row[r];
+        if (s < 0 || s >= cap)
+            return ORACLE_ERR_RANGE;
+        for (int64_t k = 0; k < row_bytes; ++k)
+            dst[r * row_bytes + k] = src[s * row_bytes + k];
+    }
+    return ORACLE_OK;
+}
+
+/*
  * Step 5a, greedy target choice per verify row [P1, "Background"]: under
  * greedy verification the target's token at a row is the vocabulary entry with
  * the largest logit; among equal maxima the lowest index is taken (a later

@@ -177,6 +177,21 @@ def test_cap_accept_validation(L):
     assert cap_call(L, sums=A + 4) == EALIGN
 
 
+def gather_call(L, src=A, psrc=A, cu=A, B=4, g=8, row_bytes=64, dst=A):
+    f = lambda x: P(x) if x else None
+    return L.dspark_gather_rows(f(src), f(psrc), f(cu), B, g, row_bytes, f(dst), None)
+
+
+def test_gather_rows_validation(L):
+    assert gather_call(L, src=0) == ENULL
+    assert gather_call(L, dst=0) == ENULL
+    assert gather_call(L, B=0) == ESHAPE
+    assert gather_call(L, row_bytes=0) == ESHAPE
+    assert gather_call(L, row_bytes=-8) == ESHAPE
+    assert gather_call(L, psrc=A + 2) == EALIGN
+    assert gather_call(L, cu=A + 1) == EALIGN
+
+
 def test_workspace_init_validation(L):
     assert L.dspark_workspace_init(None, 1024, None) == ENULL
     assert L.dspark_workspace_init(P(A + 8), 1024, None) == EALIGN

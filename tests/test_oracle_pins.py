@@ -315,6 +315,37 @@ def test_accept_known_planted_prefix(seed):
             assert bon[b] != tok[b, a + 1]
 
 
+# ---------------------------------------------------------- packed row gather
+
+@pytest.mark.parametrize("dtype,row", [(np.uint8, (13,)), (np.int32, (3, 5)), (np.uint16, (64,))])
+def test_gather_rows_against_fancy_indexing(dtype, row):
+    # Row r < cu[B] is row packed_src_row[r] of src, byte for byte; the rest
+    # of the destination keeps its contents. Catches an off-by-one row, a
+    # wrong row width and writes past the packed total.
+    rng = np.random.default_rng(7)
+    B, g = 6, 4
+    cap = B * (g + 1)
+    src = rng.integers(0, 200, (cap,) + row).astype(dtype)
+    L = rng.integers(0, g + 1, B).astype(np.int32)
+    cu, pt, ps = oracle.compact(L, np.zeros((B, g + 1), np.int32))
+    total = int(cu[-1])
+    sentinel = np.full((cap,) + row, 77, dtype)
+    out = oracle.gather_rows(src, ps, cu, dst=sentinel)
+    assert np.array_equal(out[:total], src[ps[:total]])
+    assert np.all(out[total:] == 77)
+    # the rows gathered are request b's rows 0..L_b in order
+    for b in range(B):
+        for j in range(L[b] + 1):
+            assert np.array_equal(out[cu[b] + j], src[b * (g + 1) + j])
+
+
+def test_gather_rows_rejects_bad_source_row():
+    cu = np.array([0, 2], np.int32)
+    ps = np.array([0, 9], np.int32)
+    with pytest.raises(oracle.OracleError):
+        oracle.gather_rows(np.zeros((2, 4), np.uint8), ps, cu)
+
+
 # ------------------------------------------------ static and cap-accept modes
 
 def _planted_block(rng, B, g, V):
