@@ -238,6 +238,56 @@ def run_gather(cfg, outs, steps, dspark, torch, width=7168):
                 frac_of_hbm_peak=nbytes / (us / 1e6) / 1e9 / HBM_PEAK_GBS)
 
 
+def run_graph_latency(cfg, steps, dspark, torch, make_step, make_params, R=4):
+    """Launch latency of the fused step at a small workload: K eager
+    dspark_step calls through the Python binding against K replays of HIP
+    graphs captured once per resident batch (same kernels, same buffers)."""
+    dev = torch.device("cuda:0")
+    p = make_params(cfg)
+    slots = [make_step(cfg, i, device=dev, params=p) for i in range(R)]
+    outs = [dspark.alloc_step_outputs(cfg.B, cfg.gamma, dev) for _ in slots]
+    ws = dspark.workspace(cfg.B, cfg.gamma, cfg.V, dev)
+
+    def body(i):
+        s = slots[i]
+        dspark.dspark_step(s.hidden, s.w, s.bias, s.temps, s.tokens, s.logits, cfg.mode,
+                           cutoff=s.cutoff, budget=s.budget, out=outs[i], ws=ws)
+
+    def timed(fn):
+        for i in range(2 * R):
+            fn(i % R)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0 = time.perf_counter()
+        e0.record()
+        for i in range(steps):
+            fn(i % R)
+        e1.record()
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) * 1e6 / steps, e0.elapsed_time(e1) * 1e3 / steps
+
+    eager_wall, eager_ev = timed(body)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for i in range(R):
+            body(i)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graphs = []
+    for i in range(R):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            body(i)
+        graphs.append(g)
+    torch.cuda.synchronize()
+    graph_wall, graph_ev = timed(lambda i: graphs[i].replay())
+    del graphs
+    return dict(workload=cfg.name, B=cfg.B, eager_us_per_step=eager_wall,
+                eager_event_us_per_step=eager_ev, graph_us_per_step=graph_wall,
+                graph_event_us_per_step=graph_ev)
+
+
 def stream_read_context(torch, dev):
     """HBM GB/s of a plain device-to-device copy of 1 GiB on the same device,
     for context (bytes read plus bytes written over the copy time)."""
@@ -473,6 +523,12 @@ def main():
         extra["budget_d7168_V129280_T768"] = arm_summary(cfg4, r_4, args.steps, cfg4.B)
         log(f"budget d=7168 arm: {extra['budget_d7168_V129280_T768']['rows_per_s']:.3e} rows/s")
         del slots4, outs4
+        lat = [run_graph_latency(CONFIGS[n], args.steps, dspark, torch, make_step, make_params)
+               for n in ("batch1", "mid")]
+        extra["graph_replay_latency"] = lat
+        for x in lat:
+            log(f"graph replay, {x['workload']}: eager {x['eager_us_per_step']:.1f} us/step, "
+                f"graph {x['graph_us_per_step']:.1f} us/step")
         context = stream_read_context(torch, dev)
         log(f"plain device copy: {context['gbs']:.0f} GB/s")
 

@@ -54,6 +54,7 @@ def lib() -> ctypes.CDLL:
                                   P, P, S, P]
         L.dspark_cap_accept.argtypes = [P, P, P, I, I, P, P, P, P, P]
         L.dspark_gather_rows.argtypes = [P, P, P, I, I, LL, P, P]
+        L.dspark_tier_select.argtypes = [P, I, I, P, I, ctypes.c_int32, P, P, P, P, P]
         L.dspark_workspace_bytes.argtypes = [I, I, I]
         L.dspark_workspace_bytes.restype = S
         L.dspark_workspace_init.argtypes = [P, S, P]
@@ -61,7 +62,7 @@ def lib() -> ctypes.CDLL:
         L.dspark_status_string.restype = ctypes.c_char_p
         for f in (L.dspark_confidence, L.dspark_schedule, L.dspark_compact, L.dspark_accept,
                   L.dspark_step, L.dspark_workspace_init, L.dspark_cap_accept,
-                  L.dspark_gather_rows):
+                  L.dspark_gather_rows, L.dspark_tier_select):
             f.restype = ctypes.c_int
         _lib = L
     return _lib
@@ -275,6 +276,32 @@ def dspark_gather_rows(src, packed_src_row, cu_seqlens, out=None):
     return out
 
 
+def dspark_tier_select(cu_seqlens, gamma, tiers, pad_token=0, packed_tokens=None,
+                       packed_src_row=None, out=None):
+    """Graph tier of a packed batch: (padded_total [1], tier_index [1]) int32 on
+    the device; pads packed_tokens / packed_src_row (when given) up to the
+    tier. tiers: int32 device tensor, strictly ascending."""
+    _need(cu_seqlens, "cu_seqlens", torch.int32)
+    B = cu_seqlens.numel() - 1
+    _need(tiers, "tiers", torch.int32)
+    dev = cu_seqlens.device
+    cap = B * (gamma + 1)
+    for t, n in ((packed_tokens, "packed_tokens"), (packed_src_row, "packed_src_row")):
+        if t is not None:
+            _need(t, n, torch.int32, (cap,))
+    out = out or {}
+    padded = out.get("padded_total")
+    idx = out.get("tier_index")
+    padded = torch.empty(1, dtype=torch.int32, device=dev) if padded is None else padded
+    idx = torch.empty(1, dtype=torch.int32, device=dev) if idx is None else idx
+    _need(padded, "padded_total", torch.int32, (1,))
+    _need(idx, "tier_index", torch.int32, (1,))
+    _ok("dspark_tier_select", lib().dspark_tier_select(
+        _ptr(cu_seqlens), B, int(gamma), _ptr(tiers), tiers.numel(), int(pad_token), _ptr(padded),
+        _ptr(idx), _ptr(packed_tokens), _ptr(packed_src_row), _stream(dev)))
+    return padded, idx
+
+
 def dspark_cap_accept(packed_argmax_full, tokens, lengths, out=None, sums=None):
     """Cap-accept audit arm over a static verify: (accepted, bonus,
     accepted_full, sums). packed_argmax_full holds the argmax of every row of
@@ -351,7 +378,7 @@ def dspark_step(hidden, w, bias, temps, tokens, logits, mode, cutoff=None, budge
 
 __all__ = ["DsparkError", "lib", "LIB_PATH", "dspark_status_string", "dspark_confidence", "dspark_schedule",
            "dspark_compact", "dspark_accept", "dspark_step", "dspark_cap_accept",
-           "dspark_gather_rows",
+           "dspark_gather_rows", "dspark_tier_select",
            "dspark_workspace_bytes",
            "dspark_workspace_init", "workspace", "alloc_step_outputs", "STEP_OUTPUTS",
            "DSPARK_CUT_THRESHOLD", "DSPARK_CUT_BUDGET", "DSPARK_CUT_STATIC"]

@@ -48,6 +48,7 @@ using namespace dspark;
 namespace {
 
 constexpr int kMaxD = 1 << 20;
+constexpr int kMaxTiers = 4096;
 
 inline bool misaligned(const void *p, size_t a) { return p && ((uintptr_t)p % a) != 0; }
 
@@ -150,6 +151,22 @@ DSPARK_API dspark_status dspark_gather_rows(const void *src, const int32_t *pack
     if (misaligned(packed_src_row, 4) || misaligned(cu_seqlens, 4)) return DSPARK_ERR_ALIGN;
     return launched(launch_gather_rows(src, packed_src_row, cu_seqlens, B, gamma,
                                        (int64_t)row_bytes, dst, as_stream(stream)));
+}
+
+DSPARK_API dspark_status dspark_tier_select(const int32_t *cu_seqlens, int B, int gamma,
+                                            const int32_t *tiers, int ntiers, int32_t pad_token,
+                                            int32_t *padded_total, int32_t *tier_index,
+                                            int32_t *packed_tokens, int32_t *packed_src_row,
+                                            void *stream) {
+    if (!cu_seqlens || !tiers || !padded_total || !tier_index) return DSPARK_ERR_NULL;
+    if (dspark_status st = check_bg(B, gamma)) return st;
+    if (ntiers < 1 || ntiers > kMaxTiers) return DSPARK_ERR_SHAPE;
+    if (misaligned(cu_seqlens, 4) || misaligned(tiers, 4) || misaligned(padded_total, 4) ||
+        misaligned(tier_index, 4) || misaligned(packed_tokens, 4) || misaligned(packed_src_row, 4))
+        return DSPARK_ERR_ALIGN;
+    return launched(launch_tier_select(cu_seqlens, B, gamma, tiers, ntiers, pad_token,
+                                       padded_total, tier_index, packed_tokens, packed_src_row,
+                                       as_stream(stream)));
 }
 
 DSPARK_API dspark_status dspark_accept(const dspark_bf16 *logits, const int32_t *packed_src_row,

@@ -416,8 +416,13 @@ hipError_t launch_fused_step(const uint16_t *hidden, const uint16_t *w, float bi
     p.arrivals = rcnt;
     p.target_waves = kStreamWavesPerCU * cus < kMaxWaves ? kStreamWavesPerCU * cus : (int)kMaxWaves;
     p.root_waves = root_waves;
-    // stream grid: enough workgroups for the target waves, at most the resident ones
-    const int stream_wgs_needed = (p.target_waves + kStreamThreads / kWave - 1) / (kStreamThreads / kWave);
+    // stream grid: enough workgroups for the target waves, at most the resident
+    // ones, and no more than the largest possible draft rows (every request at
+    // gamma) fill with minimum-length sub-chunks
+    int stream_wgs_needed = (p.target_waves + kStreamThreads / kWave - 1) / (kStreamThreads / kWave);
+    const int64_t max_sub = ((int64_t)B * gamma * Vv + kSubMin - 1) / kSubMin;
+    const int64_t max_wgs = (max_sub + kStreamThreads / kWave - 1) / (kStreamThreads / kWave);
+    if (max_wgs < stream_wgs_needed) stream_wgs_needed = max_wgs < 1 ? 1 : (int)max_wgs;
     int g = vvec ? stream_grid<true>(lds) : stream_grid<false>(lds);
     g = g < stream_wgs_needed ? g : stream_wgs_needed;
     if (vvec)

@@ -145,6 +145,28 @@ dspark_status dspark_compact(const int32_t *lengths, const int32_t *tokens, int 
                              dspark_bf16 *packed_logits, void *stream);
 
 /*
+ * Graph tier [P1, "Ragged verify under full CUDA graphs"]: the verify graph is
+ * keyed on the packed total rounded up to the nearest captured tier, and the
+ * packed batch is padded to that tier.
+ *   tiers [ntiers] int32 (device): the captured tier sizes, strictly
+ *     ascending (not checked on the host; 1 <= ntiers <= 4096);
+ *   tier_index[0]   = smallest t with tiers[t] >= cu_seqlens[B], or ntiers when
+ *                     no tier holds the batch;
+ *   padded_total[0] = tiers[tier_index], or cu_seqlens[B] when there is none.
+ * Rows [cu_seqlens[B], min(padded_total, B*(gamma+1))) become padding:
+ * packed_tokens = pad_token, packed_src_row = -1 (either array may be NULL).
+ * Padding rows lie past cu_seqlens[B], so dspark_gather_rows and dspark_accept
+ * never read them; a consumer that runs all padded_total rows sees source row
+ * -1 there. Every launch shape of this library is independent of the packed
+ * total, so this call, like every other entry point, can be captured in a HIP
+ * graph together with the schedule and compaction and replayed for any total.
+ */
+dspark_status dspark_tier_select(const int32_t *cu_seqlens, int B, int gamma,
+                                 const int32_t *tiers, int ntiers, int32_t pad_token,
+                                 int32_t *padded_total, int32_t *tier_index,
+                                 int32_t *packed_tokens, int32_t *packed_src_row, void *stream);
+
+/*
  * Packed row gather [P1, "Ragged verify under full CUDA graphs"]: the
  * scheduled verify tokens are front-packed into one [total_tokens, hidden]
  * buffer, the layout the target's per-row matmuls already use. Gathers rows of

@@ -50,10 +50,11 @@ def _load():
         lib.oracle_cut_static.argtypes = [I, I, P]
         lib.oracle_cap_accept.argtypes = [P, P, P, I, I, P, P, P]
         lib.oracle_gather_rows.argtypes = [P, P, P, I, I, ctypes.c_int64, P]
+        lib.oracle_tier_select.argtypes = [P, I, I, P, I, ctypes.c_int32, P, P, P, P]
         for f in (lib.oracle_confidence, lib.oracle_survival, lib.oracle_cut_threshold,
                   lib.oracle_cut_budget, lib.oracle_compact, lib.oracle_argmax_rows,
                   lib.oracle_accept, lib.oracle_step, lib.oracle_cut_static,
-                  lib.oracle_cap_accept, lib.oracle_gather_rows):
+                  lib.oracle_cap_accept, lib.oracle_gather_rows, lib.oracle_tier_select):
             f.restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -175,6 +176,22 @@ def gather_rows(src, packed_src_row, cu_seqlens, dst=None):
     _check(_load().oracle_gather_rows(_p(a), _p(ps), _p(cu), B, g, row_bytes, _p(out)),
            "gather_rows")
     return out
+
+
+def tier_select(cu_seqlens, gamma, tiers, pad_token, packed_tokens=None, packed_src_row=None):
+    """(padded_total, tier_index, packed_tokens, packed_src_row): the smallest
+    captured tier holding the packed total, and copies of the packed arrays
+    with the rows up to that tier padded."""
+    cu = _arr(cu_seqlens, np.int32)
+    B = cu.shape[0] - 1
+    t = _arr(tiers, np.int32)
+    pt = None if packed_tokens is None else np.array(packed_tokens, np.int32, copy=True)
+    ps = None if packed_src_row is None else np.array(packed_src_row, np.int32, copy=True)
+    padded = np.zeros(1, np.int32)
+    idx = np.zeros(1, np.int32)
+    _check(_load().oracle_tier_select(_p(cu), B, int(gamma), _p(t), t.shape[0], int(pad_token),
+                                      _p(padded), _p(idx), _p(pt), _p(ps)), "tier_select")
+    return int(padded[0]), int(idx[0]), pt, ps
 
 
 def argmax_rows(logits_bits, src_rows=None):

@@ -277,6 +277,45 @@ int oracle_gather_rows(const uint8_t *src, const int32_t *packed_src_row,
 }
 
 /*
+ * Graph tier of a packed batch [P1, "Ragged verify under full CUDA graphs"]:
+ * the verify graph is keyed on the packed total rounded up to the nearest
+ * captured tier, and the packed batch is padded up to that tier.
+ *   tier_index = smallest t with tiers[t] >= total (tiers ascending), or
+ *                ntiers when no captured tier holds the batch;
+ *   padded     = tiers[tier_index], or total when there is no such tier.
+ * Rows [total, min(padded, B*(gamma+1))) of the packed arrays become padding:
+ * packed_tokens = pad_token and packed_src_row = -1 (nullable arrays skipped).
+ */
+int oracle_tier_select(const int32_t *cu_seqlens, int B, int gamma, const int32_t *tiers,
+                       int ntiers, int32_t pad_token, int32_t *padded_total,
+                       int32_t *tier_index, int32_t *packed_tokens, int32_t *packed_src_row)
+{
+    if (B < 1 || gamma < 1 || ntiers < 1)
+        return ORACLE_ERR_SHAPE;
+    for (int t = 1; t < ntiers; ++t)
+        if (tiers[t] <= tiers[t - 1])
+            return ORACLE_ERR_ARG;
+    int64_t cap = (int64_t)B * (gamma + 1);
+    int64_t total = cu_seqlens[B];
+    if (total < 0 || total > cap)
+        return ORACLE_ERR_RANGE;
+    int t = 0;
+    while (t < ntiers && tiers[t] < total)
+        t += 1;
+    int64_t padded = t < ntiers ? tiers[t] : total;
+    *tier_index = t;
+    *padded_total = (int32_t)padded;
+    int64_t end = padded < cap ? padded : cap;
+    for (int64_t r = total; r < end; ++r) {
+        if (packed_tokens)
+            packed_tokens[r] = pad_token;
+        if (packed_src_row)
+            packed_src_row[r] = -1;
+    }
+    return ORACLE_OK;
+}
+
+/*
  * Step 5a, greedy target choice per verify row [P1, "Background"]: under
  * greedy verification the target's token at a row is the vocabulary entry with
  * the largest logit; among equal maxima the lowest index is taken (a later

@@ -192,6 +192,22 @@ def test_gather_rows_validation(L):
     assert gather_call(L, cu=A + 1) == EALIGN
 
 
+def tier_call(L, cu=A, B=4, g=8, tiers=A, n=3, pad=0, padded=A, idx=A, ptok=0, psrc=0):
+    f = lambda x: P(x) if x else None
+    return L.dspark_tier_select(f(cu), B, g, f(tiers), n, pad, f(padded), f(idx), f(ptok),
+                                f(psrc), None)
+
+
+def test_tier_select_validation(L):
+    assert tier_call(L, tiers=0) == ENULL
+    assert tier_call(L, idx=0) == ENULL
+    assert tier_call(L, n=0) == ESHAPE
+    assert tier_call(L, n=5000) == ESHAPE
+    assert tier_call(L, B=0) == ESHAPE
+    assert tier_call(L, tiers=A + 2) == EALIGN
+    assert tier_call(L, ptok=A + 1) == EALIGN
+
+
 def test_workspace_init_validation(L):
     assert L.dspark_workspace_init(None, 1024, None) == ENULL
     assert L.dspark_workspace_init(P(A + 8), 1024, None) == EALIGN

@@ -1,0 +1,109 @@
+"""Graph tiers and HIP-graph replay of the verify step (needs an MI355X).
+
+[P1] "DFlash to DSpark in SGLang", section "Ragged verify under full CUDA
+graphs": the verify graph is keyed on the packed total rounded up to the
+nearest captured tier. dspark_tier_select picks the tier and pads the packed
+arrays on the device; it is compared with the oracle's tier pick. Every launch
+shape of the library is independent of the packed total, so one captured graph
+of the whole step (plus the tier pick) replays correctly for any schedule:
+each replay is checked against an eager run on the same inputs, with eager
+work and synchronisations between the replays.
+"""
+import numpy as np
+import pytest
+import torch
+
+import __graft_entry__  # noqa: F401
+import confidence_scheduled_ragged_amd as dspark
+import oracle
+from synth import CONFIGS, make_step
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+
+
+def t(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_tier_select_matches_oracle(seed):
+    rng = np.random.default_rng(900 + seed)
+    B = int(rng.integers(1, 300))
+    g = int(rng.integers(1, 20))
+    cap = B * (g + 1)
+    L = rng.integers(0, g + 1, B).astype(np.int32)
+    tok = rng.integers(0, 5000, (B, g + 1)).astype(np.int32)
+    ladder = np.unique(rng.integers(1, cap + 64, int(rng.integers(1, 10)))).astype(np.int32)
+    cu, ptok, psrc, _ = dspark.dspark_compact(t(L), t(tok))
+    padded, idx = dspark.dspark_tier_select(cu, g, t(ladder), -3, ptok, psrc)
+    torch.cuda.synchronize()
+    o_cu, o_pt, o_ps = oracle.compact(L, tok)
+    # the oracle pads the oracle's own packed arrays (initialised as the binding's: -1)
+    o_pad, o_idx, o_pt2, o_ps2 = oracle.tier_select(o_cu, g, ladder, -3, o_pt, o_ps)
+    assert int(padded.item()) == o_pad and int(idx.item()) == o_idx
+    assert np.array_equal(ptok.cpu().numpy(), o_pt2)
+    assert np.array_equal(psrc.cpu().numpy(), o_ps2)
+
+
+def _copy_inputs(dst, s):
+    for k in ("hidden", "temps", "tokens", "logits", "cutoff"):
+        getattr(dst, k).copy_(getattr(s, k))
+
+
+@pytest.mark.parametrize("name", ["mixed_threshold", "mixed_budget"])
+def test_step_graph_replays_match_eager(name):
+    cfg = CONFIGS[name].scaled(B=64, V=32768)
+    steps = [make_step(cfg, i, device=DEV) for i in range(4)]
+    static = make_step(cfg, 0, device=DEV)          # the captured input buffers
+    ladder = t(np.array([64, 128, 256, 512, 1088], np.int32))
+    ws = dspark.workspace(cfg.B, cfg.gamma, cfg.V, DEV)
+    out = dspark.alloc_step_outputs(cfg.B, cfg.gamma, DEV)
+    tier = {"padded_total": torch.empty(1, dtype=torch.int32, device=DEV),
+            "tier_index": torch.empty(1, dtype=torch.int32, device=DEV)}
+
+    def body():
+        dspark.dspark_step(static.hidden, static.w, static.bias, static.temps, static.tokens,
+                           static.logits, cfg.mode, cutoff=static.cutoff, budget=static.budget,
+                           out=out, ws=ws)
+        dspark.dspark_tier_select(out["cu_seqlens"], cfg.gamma, ladder, 0, out["packed_tokens"],
+                                  out["packed_src_row"], out=tier)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        body()                                        # warm-up outside the capture
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        body()
+    torch.cuda.synchronize()
+    for rep in range(3):
+        for i, s in enumerate(steps):
+            _copy_inputs(static, s)
+            for v in out.values():
+                v.fill_(-7)
+            graph.replay()
+            torch.cuda.synchronize()
+            got = {k: v.cpu().numpy().copy() for k, v in out.items()}
+            got_tier = (int(tier["padded_total"].item()), int(tier["tier_index"].item()))
+            # eager run of the same step into fresh outputs
+            e = dspark.alloc_step_outputs(cfg.B, cfg.gamma, DEV)
+            dspark.dspark_step(s.hidden, s.w, s.bias, s.temps, s.tokens, s.logits, cfg.mode,
+                               cutoff=s.cutoff, budget=s.budget, out=e, ws=ws)
+            et = dspark.dspark_tier_select(e["cu_seqlens"], cfg.gamma, ladder, 0,
+                                           e["packed_tokens"], e["packed_src_row"])
+            torch.cuda.synchronize()
+            total = int(e["cu_seqlens"][-1].item())
+            assert got_tier == (int(et[0].item()), int(et[1].item())), (rep, i)
+            pad_end = min(got_tier[0], cfg.B * (cfg.gamma + 1))
+            for k, v in e.items():
+                ev = v.cpu().numpy()
+                if k in ("packed_tokens", "packed_src_row"):
+                    assert np.array_equal(got[k][:pad_end], ev[:pad_end]), (rep, i, k)
+                elif k == "packed_argmax":
+                    assert np.array_equal(got[k][:total], ev[:total]), (rep, i, k)
+                else:
+                    assert np.array_equal(got[k], ev), (rep, i, k)

@@ -346,6 +346,47 @@ def test_gather_rows_rejects_bad_source_row():
         oracle.gather_rows(np.zeros((2, 4), np.uint8), ps, cu)
 
 
+# ----------------------------------------------------------------- graph tiers
+
+def test_tier_select_hand_examples():
+    # tiers 64/128/256 over a capacity of 4*(63+1) = 256 rows
+    tiers = [64, 128, 256]
+    B, g = 4, 63
+    for total, want_pad, want_idx in ((100, 128, 1), (128, 128, 1), (0, 64, 0), (1, 64, 0),
+                                      (256, 256, 2), (129, 256, 2)):
+        cu = np.array([0, total, total, total, total], np.int32)
+        pt = np.full(B * (g + 1), 5, np.int32)
+        ps = np.full(B * (g + 1), 6, np.int32)
+        padded, idx, pt2, ps2 = oracle.tier_select(cu, g, tiers, -9, pt, ps)
+        assert (padded, idx) == (want_pad, want_idx)
+        assert np.all(pt2[total:want_pad] == -9) and np.all(ps2[total:want_pad] == -1)
+        assert np.all(pt2[:total] == 5) and np.all(pt2[want_pad:] == 5)
+        assert np.all(ps2[want_pad:] == 6)
+
+
+def test_tier_select_beyond_the_largest_tier_and_library_search():
+    # no captured tier holds the batch: index ntiers, nothing padded; and on
+    # random ladders the index is numpy's left insertion point
+    padded, idx, pt, _ = oracle.tier_select(np.array([0, 40], np.int32), 63, [8, 16, 32], 0,
+                                            np.zeros(64, np.int32))
+    assert (padded, idx) == (40, 3) and np.all(pt == 0)
+    rng = np.random.default_rng(5)
+    for _ in range(50):
+        tiers = np.unique(rng.integers(1, 300, rng.integers(1, 8))).astype(np.int32)
+        total = int(rng.integers(0, 300))
+        B = 5
+        g = 59
+        cu = np.array([0] + [total] * B, np.int32)
+        padded, idx, _, _ = oracle.tier_select(cu, g, tiers, 0)
+        assert idx == int(np.searchsorted(tiers, total, side="left"))
+        assert padded == (int(tiers[idx]) if idx < len(tiers) else total)
+
+
+def test_tier_select_rejects_unsorted_tiers():
+    with pytest.raises(oracle.OracleError):
+        oracle.tier_select(np.array([0, 3], np.int32), 3, [8, 8], 0)
+
+
 # ------------------------------------------------ static and cap-accept modes
 
 def _planted_block(rng, B, g, V):
