@@ -51,10 +51,13 @@ def _load():
         lib.oracle_cap_accept.argtypes = [P, P, P, I, I, P, P, P]
         lib.oracle_gather_rows.argtypes = [P, P, P, I, I, ctypes.c_int64, P]
         lib.oracle_tier_select.argtypes = [P, I, I, P, I, ctypes.c_int32, P, P, P, P]
+        lib.oracle_cut_combined.argtypes = [P, P, I, I, L, P]
+        lib.oracle_cost_cutoff.argtypes = [P, I, ctypes.c_int32, I, P]
         for f in (lib.oracle_confidence, lib.oracle_survival, lib.oracle_cut_threshold,
                   lib.oracle_cut_budget, lib.oracle_compact, lib.oracle_argmax_rows,
                   lib.oracle_accept, lib.oracle_step, lib.oracle_cut_static,
-                  lib.oracle_cap_accept, lib.oracle_gather_rows, lib.oracle_tier_select):
+                  lib.oracle_cap_accept, lib.oracle_gather_rows, lib.oracle_tier_select,
+                  lib.oracle_cut_combined, lib.oracle_cost_cutoff):
             f.restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -111,6 +114,26 @@ def cut_budget(surv, budget):
     L = np.empty(B, np.int32)
     _check(_load().oracle_cut_budget(_p(s), B, g, int(budget), _p(L)), "cut_budget")
     return L
+
+
+def cut_combined(surv, cutoff, budget):
+    """Cutoffs and budget together: the top-`budget` of the positions that pass
+    their request's cutoff."""
+    s = _arr(surv, np.float64)
+    B, g = s.shape
+    c = _arr(cutoff, np.float32)
+    assert c.shape == (B,)
+    L = np.empty(B, np.int32)
+    _check(_load().oracle_cut_combined(_p(s), _p(c), B, g, int(budget), _p(L)), "cut_combined")
+    return L
+
+
+def cost_cutoff(table, load, B):
+    """Every request's cutoff from the cost table at the step's load level."""
+    t = _arr(table, np.float32)
+    c = np.empty(B, np.float32)
+    _check(_load().oracle_cost_cutoff(_p(t), t.shape[0], int(load), int(B), _p(c)), "cost_cutoff")
+    return c
 
 
 def cut_static(B, gamma):
@@ -234,7 +257,8 @@ def step(hidden_bits, w_bits, bias, temps, tokens, logits_bits, mode, cutoff=Non
     lg = np.asarray(logits_bits)
     assert lg.dtype == np.uint16 and lg.flags.c_contiguous and lg.shape[:2] == (B, g + 1)
     V = lg.shape[-1]
-    m = {"threshold": 0, "budget": 1, "static": 2}[mode] if isinstance(mode, str) else int(mode)
+    m = ({"threshold": 0, "budget": 1, "static": 2, "combined": 3}[mode] if isinstance(mode, str)
+         else int(mode))
     c = _arr(cutoff if cutoff is not None else np.zeros(B), np.float32)
     cap = B * (g + 1)
     out = dict(conf=np.empty((B, g)), survival=np.empty((B, g)),

@@ -213,6 +213,71 @@ int oracle_cut_budget(const double *surv, int B, int gamma, long long budget,
 }
 
 /*
+ * Step 3, threshold and budget together [P1, "The confidence scheduler and
+ * verify modes" (per-request marginal cost) with "Zero-overhead scheduling and
+ * kernels" (batch-wide top-k budget)]. Reading: a drafted position is eligible
+ * when it passes its request's cutoff, S_k >= c_b (at binary32, as in
+ * oracle_cut_threshold), and the batch then verifies the T eligible positions
+ * with the largest survival (ties by lower request, then lower position), or
+ * every eligible position when there are at most T. Eligibility is a prefix of
+ * each request and survival does not increase along it, so L_b is again the
+ * count of request b's picks.
+ */
+int oracle_cut_combined(const double *surv, const float *cutoff, int B, int gamma,
+                        long long budget, int32_t *lengths)
+{
+    if (B < 1 || gamma < 1)
+        return ORACLE_ERR_SHAPE;
+    if (budget < 0)
+        return ORACLE_ERR_ARG;
+    int64_t n = (int64_t)B * gamma;
+    oracle_rank_item *items = (oracle_rank_item *)malloc((size_t)(n > 0 ? n : 1) * sizeof *items);
+    if (!items)
+        return ORACLE_ERR_SHAPE;
+    int64_t m = 0;
+    for (int64_t f = 0; f < n; ++f) {
+        if (!isfinite(surv[f])) {
+            free(items);
+            return ORACLE_ERR_NONFINITE;
+        }
+        double s = decide_binary32(surv[f]);
+        if (s >= (double)cutoff[f / gamma]) {
+            items[m].s = s;
+            items[m].flat = f;
+            m += 1;
+        }
+    }
+    qsort(items, (size_t)m, sizeof *items, oracle_rank_cmp);
+    int64_t take = budget < m ? (int64_t)budget : m;
+    for (int b = 0; b < B; ++b)
+        lengths[b] = 0;
+    for (int64_t r = 0; r < take; ++r)
+        lengths[items[r].flat / gamma] += 1;
+    free(items);
+    return ORACLE_OK;
+}
+
+/*
+ * Cost-table cutoff [P1, "The confidence scheduler and verify modes"]: the
+ * server measures how much each extra verify token adds to the step time at
+ * each load and stores it as a cost table; higher load raises the marginal
+ * cost and tightens every window together. Reading: table[j] is the marginal
+ * cost at load level j already expressed in expected tokens (the unit of the
+ * survival values), and every request of the step gets the entry of the
+ * step's load level, clamped to the table:
+ *     cutoff[b] = table[min(max(load, 0), n - 1)].
+ */
+int oracle_cost_cutoff(const float *table, int n, int32_t load, int B, float *cutoff)
+{
+    if (n < 1 || B < 1)
+        return ORACLE_ERR_SHAPE;
+    int j = load < 0 ? 0 : (load > n - 1 ? n - 1 : load);
+    for (int b = 0; b < B; ++b)
+        cutoff[b] = table[j];
+    return ORACLE_OK;
+}
+
+/*
  * Step 4, ragged compaction [P1, "Ragged verify under full CUDA graphs"]: the
  * scheduled verify rows of all requests are front-packed with no padding, and
  * a cu_seqlens array marks where each request's segment starts. Request b
@@ -432,7 +497,7 @@ int oracle_cap_accept(const int32_t *lengths, const int32_t *tokens, const int32
  * One whole step in the pages' order: confidence -> survival -> cut ->
  * compaction -> argmax over the packed rows only -> acceptance and bonus.
  * mode 0 = per-request cutoffs (cutoff[B]); mode 1 = batch budget (budget);
- * mode 2 = static (the full block).
+ * mode 2 = static (the full block); mode 3 = cutoffs and budget together.
  * logits is the dense [B, gamma+1, V] block; only packed rows are read.
  * Output buffers: conf/surv [B*gamma]; lengths/accepted/bonus [B];
  * cu_seqlens [B+1]; packed_* [B*(gamma+1)] (entries past cu[B] untouched).
@@ -455,6 +520,8 @@ int oracle_step(const uint16_t *hidden, const uint16_t *w, float bias, const flo
         rc = oracle_cut_budget(surv, B, gamma, budget, lengths);
     else if (mode == 2)
         rc = oracle_cut_static(B, gamma, lengths);
+    else if (mode == 3)
+        rc = oracle_cut_combined(surv, cutoff, B, gamma, budget, lengths);
     else
         return ORACLE_ERR_ARG;
     if (rc) return rc;

@@ -346,6 +346,74 @@ def test_gather_rows_rejects_bad_source_row():
         oracle.gather_rows(np.zeros((2, 4), np.uint8), ps, cu)
 
 
+# ------------------------------------------- combined cut and cost-table cutoff
+
+def _distinct_survival(rng, B, g):
+    p = rng.uniform(0.3, 0.99, (B, g))
+    return np.cumprod(p, axis=1)
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_combined_brute_force(seed):
+    # Among every selection that keeps a prefix of each request's eligible
+    # drafts (L_b <= threshold length) with min(T, #eligible) drafts in total,
+    # the pick must be the one of largest kept survival mass (values distinct,
+    # so the maximiser is unique). Catches a budget that ignores the cutoff,
+    # ranking ineligible positions, and a wrong total.
+    rng = np.random.default_rng(500 + seed)
+    B, g = 3, 4
+    surv = _distinct_survival(rng, B, g)
+    c = rng.uniform(0.2, 0.8, B).astype(np.float32)
+    T = int(rng.integers(0, B * g + 2))
+    Lthr = oracle.cut_threshold(surv, c)
+    want_total = min(T, int(Lthr.sum()))
+    best, best_mass = None, -1.0
+    for Ls in itertools.product(*[range(int(x) + 1) for x in Lthr]):
+        if sum(Ls) != want_total:
+            continue
+        mass = sum(surv[b, :Ls[b]].sum() for b in range(B))
+        if mass > best_mass:
+            best, best_mass = Ls, mass
+    L = oracle.cut_combined(surv, c, T)
+    assert tuple(L.tolist()) == best
+
+
+def test_combined_reduces_to_its_parts():
+    rng = np.random.default_rng(21)
+    B, g = 7, 6
+    surv = _distinct_survival(rng, B, g)
+    c = rng.uniform(0.1, 0.7, B).astype(np.float32)
+    Lthr = oracle.cut_threshold(surv, c)
+    # a budget that never binds leaves the threshold cut
+    assert np.array_equal(oracle.cut_combined(surv, c, int(Lthr.sum())), Lthr)
+    assert np.array_equal(oracle.cut_combined(surv, c, 10 ** 6), Lthr)
+    # cutoffs that pass everything leave the budget cut
+    zero = np.zeros(B, np.float32)
+    for T in (0, 5, 17, B * g):
+        assert np.array_equal(oracle.cut_combined(surv, zero, T), oracle.cut_budget(surv, T))
+    # cutoffs above 1 pass nothing; each window never exceeds its threshold window
+    assert np.all(oracle.cut_combined(surv, np.full(B, 2.0, np.float32), 30) == 0)
+    for T in range(0, B * g + 1, 5):
+        L = oracle.cut_combined(surv, c, T)
+        assert np.all(L <= Lthr) and L.sum() == min(T, Lthr.sum())
+
+
+def test_cost_cutoff_hand_example_and_tightening():
+    table = np.array([0.1, 0.2, 0.3], np.float32)
+    for load, want in ((-1, 0.1), (0, 0.1), (1, 0.2), (2, 0.3), (7, 0.3)):
+        c = oracle.cost_cutoff(table, load, 4)
+        assert c.dtype == np.float32 and np.all(c == np.float32(want))
+    # a cost that rises with load tightens every window together
+    rng = np.random.default_rng(3)
+    surv = _distinct_survival(rng, 9, 8)
+    prev = None
+    for load in range(3):
+        L = oracle.cut_threshold(surv, oracle.cost_cutoff(table, load, 9))
+        if prev is not None:
+            assert np.all(L <= prev)
+        prev = L
+
+
 # ----------------------------------------------------------------- graph tiers
 
 def test_tier_select_hand_examples():
