@@ -78,7 +78,7 @@ def step_bytes(cfg, total: int) -> int:
     B, g, d, V = cfg.B, cfg.gamma, cfg.d, cfg.V
     reads = (2 * B * g * d            # hidden states
              + 2 * d + 4 * g          # head weight, temperatures
-             + (4 * B if cfg.mode == "threshold" else 0)   # cutoffs
+             + (4 * B if cfg.mode in ("threshold", "combined") else 0)   # cutoffs
              + 4 * B * (g + 1)        # verify-block tokens
              + 2 * V * total)         # packed logit rows
     writes = (8 * B * g               # conf, survival
@@ -93,7 +93,7 @@ def step_bytes_a3_a6(cfg, total: int) -> int:
     curves: survival and cutoffs in, the packed logit rows, tokens, and every
     integer output."""
     B, g, V = cfg.B, cfg.gamma, cfg.V
-    reads = (4 * B * g + (4 * B if cfg.mode == "threshold" else 0)
+    reads = (4 * B * g + (4 * B if cfg.mode in ("threshold", "combined") else 0)
              + 4 * B * (g + 1) + 2 * V * total)
     writes = 4 * B + 4 * (B + 1) + 12 * total + 8 * B
     return reads + writes
@@ -199,9 +199,62 @@ def run_audit(cfg_t, cfg_b, slots, ws, steps, warmup, dspark, torch):
             full_sum += f
         tot[cfg.mode] = acc_sum / max(full_sum, 1)
     res["cap_accept_us"] = 1e3 * sorted(cap_ms)[len(cap_ms) // 2]
+    # offline STS fit on the audit records: head logits from the logged scores
+    # and the temperatures they were taken with, labels from cap-accept
+    from confidence_scheduled_ragged_amd.calibrate import (fit_sts_temperatures,
+                                                           head_logits_from_scores)
+    import numpy as np
+    zs, fulls = [], []
+    for i, s in enumerate(slots):
+        _, _, full, _ = dspark.dspark_cap_accept(outs_s[i]["packed_argmax"], s.tokens,
+                                                 outs_s[i]["lengths"])
+        zs.append(head_logits_from_scores(outs_s[i]["conf"].cpu().numpy(),
+                                          s.temps.cpu().numpy()))
+        fulls.append(full.cpu().numpy())
+    t0 = time.perf_counter()
+    fitted = fit_sts_temperatures(np.concatenate(zs), np.concatenate(fulls))
+    res["sts_fit"] = dict(records=int(sum(len(f) for f in fulls)),
+                          ms=(time.perf_counter() - t0) * 1e3,
+                          temperatures=[round(float(x), 4) for x in fitted],
+                          head_temperatures=[round(float(x), 4)
+                                             for x in slots[0].temps.cpu().numpy()])
     res["utilization_threshold_window"] = tot["threshold"]
     res["utilization_budget_window"] = tot["budget"]
     return res
+
+
+def run_combined_cost_table(cfg_c, slots, ws, steps, warmup, dspark, torch):
+    """The cutoff from a cost table on the device (load level 3 of a five-entry
+    table, 0.25 expected tokens) and the cutoff and budget together (T = 742)
+    in one fused step, on the resident mixed batches."""
+    dev = slots[0].hidden.device
+    table = torch.tensor([0.1, 0.15, 0.2, 0.25, 0.3], dtype=torch.float32, device=dev)
+    load = torch.tensor([3], dtype=torch.int32, device=dev)
+    cut = torch.empty(cfg_c.B, dtype=torch.float32, device=dev)
+    R = len(slots)
+    outs = [dspark.alloc_step_outputs(cfg_c.B, cfg_c.gamma, dev) for _ in slots]
+
+    def launch(i):
+        s = slots[i % R]
+        dspark.dspark_cost_cutoff(table, load, cfg_c.B, cutoff=cut)
+        dspark.dspark_step(s.hidden, s.w, s.bias, s.temps, s.tokens, s.logits, "combined",
+                           cutoff=cut, budget=cfg_c.budget, out=outs[i % R], ws=ws)
+
+    for i in range(max(warmup, 2 * R)):
+        launch(i)
+    torch.cuda.synchronize()
+    totals = [int(o["cu_seqlens"][-1].item()) for o in outs]
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(steps):
+        launch(i)
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / steps
+    nbytes = sum(step_bytes(cfg_c, totals[i % R]) for i in range(steps)) / steps
+    return dict(us_per_step=us, mean_packed_rows=sum(totals) / R, budget=cfg_c.budget,
+                cutoff=0.25, achieved_gbs=nbytes / (us / 1e6) / 1e9,
+                frac_of_hbm_peak=nbytes / (us / 1e6) / 1e9 / HBM_PEAK_GBS)
 
 
 def run_gather(cfg, outs, steps, dspark, torch, width=7168):
@@ -509,6 +562,11 @@ def main():
         r_b = run_arm(cfg_b, slots, outs, ws, args.steps, args.warmup, dspark, torch)
         extra["mixed_budget_T742"] = arm_summary(cfg_b, r_b, args.steps, cfg_b.B)
         log(f"budget arm: {extra['mixed_budget_T742']['rows_per_s']:.3e} rows/s")
+        cc = run_combined_cost_table(CONFIGS["mixed_combined"], slots, ws, args.steps,
+                                     args.warmup, dspark, torch)
+        extra["combined_cost_table"] = cc
+        log(f"cost table + combined cut: {cc['us_per_step']:.1f} us/step, "
+            f"{cc['mean_packed_rows']:.0f} rows")
         audit = run_audit(cfg_t, cfg_b, slots, ws, args.steps, args.warmup, dspark, torch)
         extra["audit_static_cap_accept"] = audit
         log(f"audit: static {audit['static_full_block']['event_ms_per_step'] * 1e3:.1f} us/step, "

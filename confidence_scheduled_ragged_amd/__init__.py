@@ -22,8 +22,9 @@ LIB_PATH = os.path.join(_HERE, "libdspark.so")
 DSPARK_CUT_THRESHOLD = 0
 DSPARK_CUT_BUDGET = 1
 DSPARK_CUT_STATIC = 2
+DSPARK_CUT_COMBINED = 3
 MODES = {"threshold": DSPARK_CUT_THRESHOLD, "budget": DSPARK_CUT_BUDGET,
-         "static": DSPARK_CUT_STATIC}
+         "static": DSPARK_CUT_STATIC, "combined": DSPARK_CUT_COMBINED}
 
 _lib = None
 
@@ -55,6 +56,7 @@ def lib() -> ctypes.CDLL:
         L.dspark_cap_accept.argtypes = [P, P, P, I, I, P, P, P, P, P]
         L.dspark_gather_rows.argtypes = [P, P, P, I, I, LL, P, P]
         L.dspark_tier_select.argtypes = [P, I, I, P, I, ctypes.c_int32, P, P, P, P, P]
+        L.dspark_cost_cutoff.argtypes = [P, I, P, I, P, P]
         L.dspark_workspace_bytes.argtypes = [I, I, I]
         L.dspark_workspace_bytes.restype = S
         L.dspark_workspace_init.argtypes = [P, S, P]
@@ -62,7 +64,7 @@ def lib() -> ctypes.CDLL:
         L.dspark_status_string.restype = ctypes.c_char_p
         for f in (L.dspark_confidence, L.dspark_schedule, L.dspark_compact, L.dspark_accept,
                   L.dspark_step, L.dspark_workspace_init, L.dspark_cap_accept,
-                  L.dspark_gather_rows, L.dspark_tier_select):
+                  L.dspark_gather_rows, L.dspark_tier_select, L.dspark_cost_cutoff):
             f.restype = ctypes.c_int
         _lib = L
     return _lib
@@ -276,6 +278,19 @@ def dspark_gather_rows(src, packed_src_row, cu_seqlens, out=None):
     return out
 
 
+def dspark_cost_cutoff(table, load, B, cutoff=None):
+    """Every request's cutoff from the cost table at the step's load level:
+    table fp32 [n] and load int32 [1] on the device; returns cutoff fp32 [B]."""
+    _need(table, "table", torch.float32)
+    _need(load, "load", torch.int32, (1,))
+    dev = table.device
+    cutoff = torch.empty(B, dtype=torch.float32, device=dev) if cutoff is None else cutoff
+    _need(cutoff, "cutoff", torch.float32, (B,))
+    _ok("dspark_cost_cutoff", lib().dspark_cost_cutoff(
+        _ptr(table), table.numel(), _ptr(load), int(B), _ptr(cutoff), _stream(dev)))
+    return cutoff
+
+
 def dspark_tier_select(cu_seqlens, gamma, tiers, pad_token=0, packed_tokens=None,
                        packed_src_row=None, out=None):
     """Graph tier of a packed batch: (padded_total [1], tier_index [1]) int32 on
@@ -378,7 +393,8 @@ def dspark_step(hidden, w, bias, temps, tokens, logits, mode, cutoff=None, budge
 
 __all__ = ["DsparkError", "lib", "LIB_PATH", "dspark_status_string", "dspark_confidence", "dspark_schedule",
            "dspark_compact", "dspark_accept", "dspark_step", "dspark_cap_accept",
-           "dspark_gather_rows", "dspark_tier_select",
+           "dspark_gather_rows", "dspark_tier_select", "dspark_cost_cutoff",
            "dspark_workspace_bytes",
            "dspark_workspace_init", "workspace", "alloc_step_outputs", "STEP_OUTPUTS",
-           "DSPARK_CUT_THRESHOLD", "DSPARK_CUT_BUDGET", "DSPARK_CUT_STATIC"]
+           "DSPARK_CUT_THRESHOLD", "DSPARK_CUT_BUDGET", "DSPARK_CUT_STATIC",
+           "DSPARK_CUT_COMBINED"]

@@ -59,7 +59,16 @@ inline dspark_status check_bg(int B, int gamma) {
 }
 
 inline bool valid_mode(int mode) {
-    return mode == DSPARK_CUT_THRESHOLD || mode == DSPARK_CUT_BUDGET || mode == DSPARK_CUT_STATIC;
+    return mode == DSPARK_CUT_THRESHOLD || mode == DSPARK_CUT_BUDGET ||
+           mode == DSPARK_CUT_STATIC || mode == DSPARK_CUT_COMBINED;
+}
+
+inline bool needs_cutoff(int mode) {
+    return mode == DSPARK_CUT_THRESHOLD || mode == DSPARK_CUT_COMBINED;
+}
+
+inline bool needs_budget(int mode) {
+    return mode == DSPARK_CUT_BUDGET || mode == DSPARK_CUT_COMBINED;
 }
 
 inline dspark_status launched(hipError_t e) { return e == hipSuccess ? DSPARK_OK : DSPARK_ERR_HIP; }
@@ -110,10 +119,10 @@ DSPARK_API dspark_status dspark_schedule(const float *survival, int B, int gamma
                                          const float *cutoff, long long budget, int32_t *lengths,
                                          void *stream) {
     if (!survival || !lengths) return DSPARK_ERR_NULL;
-    if (mode == DSPARK_CUT_THRESHOLD && !cutoff) return DSPARK_ERR_NULL;
+    if (needs_cutoff(mode) && !cutoff) return DSPARK_ERR_NULL;
     if (dspark_status st = check_bg(B, gamma)) return st;
     if (!valid_mode(mode)) return DSPARK_ERR_ARG;
-    if (mode == DSPARK_CUT_BUDGET && budget < 0) return DSPARK_ERR_ARG;
+    if (needs_budget(mode) && budget < 0) return DSPARK_ERR_ARG;
     if (misaligned(survival, 4) || misaligned(cutoff, 4) || misaligned(lengths, 4))
         return DSPARK_ERR_ALIGN;
     return launched(launch_schedule(survival, B, gamma, mode, cutoff, budget, lengths,
@@ -169,6 +178,15 @@ DSPARK_API dspark_status dspark_tier_select(const int32_t *cu_seqlens, int B, in
                                        as_stream(stream)));
 }
 
+DSPARK_API dspark_status dspark_cost_cutoff(const float *table, int n, const int32_t *load,
+                                            int B, float *cutoff, void *stream) {
+    if (!table || !load || !cutoff) return DSPARK_ERR_NULL;
+    if (n < 1 || B < 1 || B > DSPARK_MAX_ROWS) return DSPARK_ERR_SHAPE;
+    if (misaligned(table, 4) || misaligned(load, 4) || misaligned(cutoff, 4))
+        return DSPARK_ERR_ALIGN;
+    return launched(launch_cost_cutoff(table, n, load, B, cutoff, as_stream(stream)));
+}
+
 DSPARK_API dspark_status dspark_accept(const dspark_bf16 *logits, const int32_t *packed_src_row,
                                        const int32_t *cu_seqlens, const int32_t *tokens, int B,
                                        int gamma, int V, int32_t *packed_argmax, int32_t *accepted,
@@ -213,11 +231,11 @@ DSPARK_API dspark_status dspark_step(const dspark_bf16 *hidden, const dspark_bf1
     if (!hidden || !w || !temps || !tokens || !logits || !lengths || !cu_seqlens ||
         !packed_tokens || !packed_src_row || !packed_argmax || !accepted || !bonus || !ws)
         return DSPARK_ERR_NULL;
-    if (mode == DSPARK_CUT_THRESHOLD && !cutoff) return DSPARK_ERR_NULL;
+    if (needs_cutoff(mode) && !cutoff) return DSPARK_ERR_NULL;
     if (dspark_status st = check_bg(B, gamma)) return st;
     if (d < 1 || d > kMaxD || V < 1) return DSPARK_ERR_SHAPE;
     if (!valid_mode(mode)) return DSPARK_ERR_ARG;
-    if (mode == DSPARK_CUT_BUDGET && budget < 0) return DSPARK_ERR_ARG;
+    if (needs_budget(mode) && budget < 0) return DSPARK_ERR_ARG;
     if (!std::isfinite(bias)) return DSPARK_ERR_ARG;
     if (misaligned(hidden, 2) || misaligned(w, 2) || misaligned(temps, 4) ||
         misaligned(tokens, 4) || misaligned(logits, 2) || misaligned(cutoff, 4) ||

@@ -148,6 +148,8 @@ hipError_t launch_cap_accept(const int32_t *pam_full, const int32_t *tokens,
 hipError_t launch_tier_select(const int32_t *cu, int B, int gamma, const int32_t *tiers,
                               int ntiers, int32_t pad_token, int32_t *padded_total,
                               int32_t *tier_index, int32_t *ptok, int32_t *psrc, hipStream_t s);
+hipError_t launch_cost_cutoff(const float *table, int n, const int32_t *load, int B,
+                              float *cutoff, hipStream_t s);
 hipError_t launch_fused_step(const uint16_t *hidden, const uint16_t *w, float bias,
                              const float *temps, const int32_t *tokens, const uint16_t *logits,
                              int B, int gamma, int d, int V, int mode, const float *cutoff,

@@ -52,7 +52,7 @@ struct FrontParams {
     const float *temps, *cutoff;
     float bias;
     int B, gamma, d, V, mode;
-    int t;                // budget mode: number of positions to pick, in [0, B*gamma]
+    int t;                // budget / combined: number of positions to pick, in [0, B*gamma]
     float *conf, *surv;
     int32_t *lengths;
     uint64_t *rkeys;      // segment keys of the root rows
@@ -154,15 +154,25 @@ __global__ __launch_bounds__(kFrontThreads) void step_front_kernel(FrontParams p
     const int N = p.B * p.gamma;
     float *sv = reinterpret_cast<float *>(dyn_lds);  // w is no longer needed
     __syncthreads();
-    for (int f = tid; f < N; f += bd)
-        sv[f] = __hip_atomic_load(p.surv + f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __syncthreads();
-    if (p.t <= 0 || p.t >= N) {
-        for (int r = tid; r < p.B; r += bd) p.lengths[r] = p.t <= 0 ? 0 : p.gamma;
+    // combined cut: a position below its request's cutoff ranks below every
+    // eligible one, and the budget is capped by the eligible count
+    const bool combined = p.mode == DSPARK_CUT_COMBINED;
+    int n = 0;
+    for (int f = tid; f < N; f += bd) {
+        float v = __hip_atomic_load(p.surv + f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (combined && !(v >= p.cutoff[f / p.gamma])) v = -INFINITY;
+        else ++n;
+        sv[f] = v;
+    }
+    int eligible;
+    block_excl_scan(n, &eligible, scan_lds);  // contains the barriers sv needs
+    const int t = p.t < eligible ? p.t : eligible;
+    if (t <= 0 || t >= N) {
+        for (int r = tid; r < p.B; r += bd) p.lengths[r] = t <= 0 ? 0 : p.gamma;
         return;
     }
-    const BudgetCut cut = budget_select_runs<kFusedSelPer>(sv, N, p.t, hist, sh);
-    budget_lengths(sv, p.B, p.gamma, cut, p.lengths, scan_lds);
+    const BudgetCut cut = budget_select_runs<kFusedSelPer>(sv, N, t, hist, sh);
+    budget_lengths(sv, nullptr, p.B, p.gamma, cut, p.lengths, scan_lds);
 }
 
 // ----------------------------------------------------------------- stream
@@ -351,7 +361,8 @@ hipError_t launch_fused_step(const uint16_t *hidden, const uint16_t *w, float bi
     const int N = B * gamma;
     const bool hvec = (d % 8 == 0) && (((uintptr_t)hidden | (uintptr_t)w) % 16 == 0);
     const bool ldsw = hvec && d <= kFrontMaxLdsW;
-    const bool select_in_front = mode == DSPARK_CUT_BUDGET && N <= kFusedSelMax;
+    const bool select_in_front =
+        (mode == DSPARK_CUT_BUDGET || mode == DSPARK_CUT_COMBINED) && N <= kFusedSelMax;
     const bool vvec = (V % 8 == 0) && ((uintptr_t)logits % 16 == 0);
     FrontParams fp;
     fp.hidden = hidden;
@@ -392,7 +403,7 @@ hipError_t launch_fused_step(const uint16_t *hidden, const uint16_t *w, float bi
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
 
-    if (mode == DSPARK_CUT_BUDGET && !select_in_front) {
+    if ((mode == DSPARK_CUT_BUDGET || mode == DSPARK_CUT_COMBINED) && !select_in_front) {
         e = launch_schedule(surv, B, gamma, mode, cutoff, budget, lengths, s);
         if (e != hipSuccess) return e;
     }

@@ -38,6 +38,28 @@ __device__ __forceinline__ int block_excl_scan(int x, int *total, int *lds) {
     return r;
 }
 
+// Survival of flat position f as the budget ranks it. With per-request
+// cutoffs (the combined cut) a position below its request's cutoff ranks below
+// every eligible one (-inf); without, the survival itself.
+__device__ __forceinline__ float ranked_value(const float *__restrict__ surv,
+                                              const float *__restrict__ cutoff, int gamma,
+                                              int f) {
+    const float v = surv[f];
+    return (cutoff && !(v >= cutoff[f / gamma])) ? -INFINITY : v;
+}
+
+// Number of positions of [0, N) that pass their request's cutoff, summed over
+// the block (every thread calls it and gets the total). lds needs 17 ints.
+__device__ __forceinline__ int block_count_eligible(const float *__restrict__ surv,
+                                                    const float *__restrict__ cutoff, int gamma,
+                                                    int N, int *lds) {
+    int n = 0;
+    for (int f = threadIdx.x; f < N; f += blockDim.x) n += surv[f] >= cutoff[f / gamma] ? 1 : 0;
+    int total;
+    block_excl_scan(n, &total, lds);
+    return total;
+}
+
 // Threshold cut of one request: number of positions with survival >= c.
 // A NaN c makes every comparison false.
 __device__ __forceinline__ int threshold_length(const float *s, int gamma, float c) {
@@ -59,8 +81,10 @@ struct BudgetCut {
 
 constexpr int kSelCache = 8;  // values cached per thread between passes
 
-__device__ __forceinline__ BudgetCut budget_select(const float *__restrict__ surv, int N, int t,
-                                                   uint32_t *hist /*256*/, uint32_t *sh /*2*/) {
+__device__ __forceinline__ BudgetCut budget_select(const float *__restrict__ surv,
+                                                   const float *__restrict__ cutoff, int gamma,
+                                                   int N, int t, uint32_t *hist /*256*/,
+                                                   uint32_t *sh /*2*/) {
     const int tid = threadIdx.x;
     const int bd = blockDim.x;
     const int lane = tid & (kWave - 1);
@@ -68,7 +92,7 @@ __device__ __forceinline__ BudgetCut budget_select(const float *__restrict__ sur
 #pragma unroll
     for (int j = 0; j < kSelCache; ++j) {
         int f = tid + j * bd;
-        cache[j] = f < N ? ordered_f32(surv[f]) : 0u;
+        cache[j] = f < N ? ordered_f32(ranked_value(surv, cutoff, gamma, f)) : 0u;
     }
     uint32_t prefix = 0, mask = 0;
     uint32_t remaining = (uint32_t)t;
@@ -82,7 +106,7 @@ __device__ __forceinline__ BudgetCut budget_select(const float *__restrict__ sur
             if (f < N && (u & mask) == prefix) atomicAdd(&hist[(u >> shift) & 255u], 1u);
         }
         for (int f = tid + kSelCache * bd; f < N; f += bd) {
-            uint32_t u = ordered_f32(surv[f]);
+            uint32_t u = ordered_f32(ranked_value(surv, cutoff, gamma, f));
             if ((u & mask) == prefix) atomicAdd(&hist[(u >> shift) & 255u], 1u);
         }
         __syncthreads();
@@ -196,17 +220,18 @@ __device__ __forceinline__ BudgetCut budget_select_runs(const float *__restrict_
 
 // Lengths from a budget cut for requests [0, B): L_b = #{v > tau} + the
 // request's share of the `need` tied picks, handed out in request order.
-// Every thread calls it. lds needs 17 ints.
-__device__ __forceinline__ void budget_lengths(const float *__restrict__ surv, int B, int gamma,
+// Values are ranked as budget_select ranks them (cutoff nullable). Every
+// thread calls it. lds needs 17 ints.
+__device__ __forceinline__ void budget_lengths(const float *__restrict__ surv,
+                                               const float *__restrict__ cutoff, int B, int gamma,
                                                BudgetCut cut, int32_t *lengths, int *lds) {
     int carry = 0;
     for (int base = 0; base < B; base += blockDim.x) {
         int b = base + threadIdx.x;
         int gt = 0, eq = 0;
         if (b < B) {
-            const float *s = surv + (size_t)b * gamma;
             for (int k = 0; k < gamma; ++k) {
-                uint32_t u = ordered_f32(s[k]);
+                uint32_t u = ordered_f32(ranked_value(surv, cutoff, gamma, b * gamma + k));
                 gt += u > cut.tau ? 1 : 0;
                 eq += u == cut.tau ? 1 : 0;
             }

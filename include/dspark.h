@@ -6,7 +6,8 @@
  * block of gamma tokens, runs as:
  *   1. confidence head with per-position temperature  (dspark_confidence)
  *   2. survival curve, the running product of scores   (dspark_confidence)
- *   3. verify-length cut, per request or batch budget   (dspark_schedule)
+ *   3. verify-length cut, per request or batch budget   (dspark_schedule; the
+ *      per-request cutoffs may come from a cost table:  dspark_cost_cutoff)
  *   4. ragged compaction into a packed verify batch     (dspark_compact,
  *      and dspark_gather_rows for per-position activations)
  *   5. greedy acceptance against the target's argmax    (dspark_accept)
@@ -82,7 +83,8 @@ typedef enum dspark_status {
 typedef enum dspark_cut_mode {
     DSPARK_CUT_THRESHOLD = 0, /* per-request marginal cost cutoff[b] */
     DSPARK_CUT_BUDGET = 1,    /* batch-wide budget of `budget` drafted positions */
-    DSPARK_CUT_STATIC = 2     /* the full block: L_b = gamma (no-trim baseline) */
+    DSPARK_CUT_STATIC = 2,    /* the full block: L_b = gamma (no-trim baseline) */
+    DSPARK_CUT_COMBINED = 3   /* cutoff[b] and the budget together */
 } dspark_cut_mode;
 
 #define DSPARK_MAX_GAMMA 256
@@ -120,6 +122,11 @@ dspark_status dspark_confidence(const dspark_bf16 *hidden, const dspark_bf16 *w,
  *   DSPARK_CUT_STATIC [P1, "The confidence scheduler and verify modes"]: the
  *     static verify mode, L_b = gamma for every request; survival is not read,
  *     `cutoff` and `budget` are ignored.
+ *   DSPARK_CUT_COMBINED: a position is eligible when survival[b,k-1] >=
+ *     cutoff[b]; the batch keeps the first min(budget, #eligible) eligible
+ *     positions in the budget's ranking (survival descending, then lower
+ *     request, then lower position). Eligibility is a prefix of each request,
+ *     so L_b never exceeds its threshold length. cutoff [B] and budget >= 0.
  * survival [B, gamma] fp32 (finite); lengths [B] int32 output.
  */
 dspark_status dspark_schedule(const float *survival, int B, int gamma, int mode,
@@ -181,6 +188,20 @@ dspark_status dspark_tier_select(const int32_t *cu_seqlens, int B, int gamma,
 dspark_status dspark_gather_rows(const void *src, const int32_t *packed_src_row,
                                  const int32_t *cu_seqlens, int B, int gamma, long long row_bytes,
                                  void *dst, void *stream);
+
+/*
+ * Cost-table cutoff [P1, "The confidence scheduler and verify modes"]: the
+ * server stores the marginal cost of one more verify token per load level as
+ * a cost table, and higher load tightens every window together.
+ *   cutoff[b] = table[min(max(load[0], 0), n - 1)]   for b in [0, B)
+ * table [n] fp32 (device): marginal costs in expected tokens, the unit the
+ * survival values are compared in; load [1] int32 (device): the step's load
+ * level, e.g. a bucket of the running batch, so the lookup stays on the
+ * device with the rest of the step. cutoff [B] fp32 output, ready for
+ * DSPARK_CUT_THRESHOLD or DSPARK_CUT_COMBINED.
+ */
+dspark_status dspark_cost_cutoff(const float *table, int n, const int32_t *load, int B,
+                                 float *cutoff, void *stream);
 
 /*
  * Steps 5-6 [P1, "Background"]: greedy verification commits the longest

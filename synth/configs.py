@@ -20,7 +20,7 @@ class Config:
     V: int
     bias: float                # scalar bias of the confidence head
     temp_slope: float          # STS temperatures T_i = 1 + temp_slope * i, i = 0..gamma-1
-    mode: str                  # "threshold" or "budget"
+    mode: str                  # "threshold", "budget", "static" or "combined"
     cutoff: Optional[float] = None              # fixed per-request cutoff c
     cutoff_range: Optional[Tuple[float, float]] = None  # c_b ~ U[lo, hi] per request and step
     budget_per_request: Optional[float] = None  # T = floor(budget_per_request * B)
@@ -33,7 +33,7 @@ class Config:
 
     @property
     def budget(self) -> int:
-        if self.mode != "budget":
+        if self.mode not in ("budget", "combined"):
             return 0
         return int(self.budget_per_request * self.B)
 
@@ -73,6 +73,12 @@ CONFIGS = {
                            V=151936, bias=0.0, temp_slope=0.03, mode="budget",
                            budget_per_request=2.9, logit_var=2.0, shift="bimodal",
                            match="bimodal", steps=100),
+    # The same mixed traffic under the cutoff and the budget together (the same
+    # seed stream as the two arms above, so the same batches).
+    "mixed_combined": Config(name="mixed_combined", index=5, B=256, gamma=16, d=4096,
+                             V=151936, bias=0.0, temp_slope=0.03, mode="combined",
+                             cutoff=0.25, budget_per_request=2.9, logit_var=2.0,
+                             shift="bimodal", match="bimodal", steps=100),
 }
 
 

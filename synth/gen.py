@@ -173,7 +173,7 @@ def make_step(cfg: Config, step: int, device="cpu", params: Optional[Params] = N
     s = _shift(cfg, _rng(cfg, step, 1))
     zeta = _rng(cfg, step, 2).standard_normal((B, g)) if cfg.latent else np.zeros((B, g))
     lam = s[:, None] + zeta
-    if cfg.mode == "threshold":
+    if cfg.mode in ("threshold", "combined"):
         if cfg.cutoff_range is not None:
             lo, hi = cfg.cutoff_range
             cutoff = _rng(cfg, step, 3).uniform(lo, hi, B).astype(np.float32)

@@ -64,6 +64,23 @@ def oracle_front(h: HostStep):
     if h.cfg.mode == "threshold":
         L = oracle.cut_threshold(surv, h.cutoff)
         amb = np.abs(surv - h.cutoff.astype(np.float64)[:, None]) <= BAND
+    elif h.cfg.mode == "combined":
+        L = oracle.cut_combined(surv, h.cutoff, h.budget)
+        c = h.cutoff.astype(np.float64)[:, None]
+        amb = np.abs(surv - c) <= BAND
+        elig = np.sort(surv[surv >= c])[::-1]
+        t = min(h.budget, elig.size)
+        if 0 < t < elig.size:
+            tau = elig[t - 1]
+            near_cut = amb.copy()
+            amb |= np.abs(surv - tau) <= BAND
+            # a position that may or may not pass its cutoff and would rank
+            # inside the budget can move the budget's last pick to any request
+            if np.any(near_cut & (surv >= tau - BAND)):
+                amb[:] = True
+    elif h.cfg.mode == "static":
+        L = oracle.cut_static(h.cfg.B, h.cfg.gamma)
+        amb = np.zeros_like(surv, dtype=bool)
     else:
         L = oracle.cut_budget(surv, h.budget)
         n = surv.size

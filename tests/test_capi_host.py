@@ -92,8 +92,10 @@ def test_schedule_validation(L):
     assert sched_call(L, lengths=0) == ENULL
     assert sched_call(L, cutoff=0, mode=0) == ENULL
     assert sched_call(L, B=-1) == ESHAPE
-    assert sched_call(L, mode=3, cutoff=0) == EARG
+    assert sched_call(L, mode=4, cutoff=0) == EARG
     assert sched_call(L, mode=-1, cutoff=0) == EARG
+    assert sched_call(L, mode=3, cutoff=0) == ENULL         # combined needs the cutoffs
+    assert sched_call(L, mode=3, budget=-1) == EARG         # and a budget
     assert sched_call(L, mode=1, cutoff=0, budget=-1) == EARG
     assert sched_call(L, lengths=A + 1) == EALIGN
     assert sched_call(L, mode=1, cutoff=0, surv=A + 2) == EALIGN
@@ -206,6 +208,14 @@ def test_tier_select_validation(L):
     assert tier_call(L, B=0) == ESHAPE
     assert tier_call(L, tiers=A + 2) == EALIGN
     assert tier_call(L, ptok=A + 1) == EALIGN
+
+
+def test_cost_cutoff_validation(L):
+    f = lambda x: P(x) if x else None
+    assert L.dspark_cost_cutoff(None, 3, f(A), 4, f(A), None) == ENULL
+    assert L.dspark_cost_cutoff(f(A), 0, f(A), 4, f(A), None) == ESHAPE
+    assert L.dspark_cost_cutoff(f(A), 3, f(A), 0, f(A), None) == ESHAPE
+    assert L.dspark_cost_cutoff(f(A), 3, f(A + 2), 4, f(A), None) == EALIGN
 
 
 def test_workspace_init_validation(L):
