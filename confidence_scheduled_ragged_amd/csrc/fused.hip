@@ -44,6 +44,14 @@ constexpr int kFrontRootWGsPerCU = 1;  // root-row workgroups of the front grid 
 constexpr int kStreamThreads = 512;
 constexpr int kStreamWavesPerCU = 16;  // target waves of the draft-row stream per CU
 constexpr int kStreamUnroll = 2;  // 16-byte loads in flight per lane (more waves, fewer bytes each)
+// Root rows of the front kernel: with no pick in the front (per-request cutoff,
+// static) the root rows are its critical path and get four loads in flight per
+// lane; when the front's last workgroup also runs the batch-wide pick, the
+// GEMV and pick chain is critical and the roots take two, leaving bandwidth to
+// the GEMV (measured: 110.5 against 113.4 us per step at the mixed workload's
+// threshold arm, 70.2 against 72.3 at its budget arm).
+constexpr int kRootUnrollAlone = 4;
+constexpr int kRootUnrollWithPick = 2;
 
 // ------------------------------------------------------------------ front
 
@@ -64,7 +72,7 @@ struct FrontParams {
 // cut into sub-chunks of about equal length, one per root wave: wave w of
 // nwaves streams sub-chunks w, w + nwaves, ... and leaves one key per row
 // segment at rkeys[s + b].
-template <bool kVec>
+template <bool kVec, int kRootUnroll>
 __device__ __forceinline__ void front_root_rows(const FrontParams &p, int64_t w, int64_t nwaves) {
     const int lane = threadIdx.x & (kWave - 1);
     const int64_t Vv = kVec ? (p.V >> 3) : p.V;
@@ -81,7 +89,7 @@ __device__ __forceinline__ void front_root_rows(const FrontParams &p, int64_t w,
             const int64_t seg_end = e_end < row_end ? e_end : row_end;
             float best = -INFINITY;
             int bidx = -1;
-            lane_row_segment<kVec, kStreamUnroll>(p.logits + (size_t)r * row_stride, e - r * Vv,
+            lane_row_segment<kVec, kRootUnroll>(p.logits + (size_t)r * row_stride, e - r * Vv,
                                                   seg_end - r * Vv, lane, best, bidx);
             uint64_t key = bidx >= 0 ? argmax_key(best, (uint32_t)bidx) : 0ull;
             key = wave_max_u64(key);
@@ -92,7 +100,7 @@ __device__ __forceinline__ void front_root_rows(const FrontParams &p, int64_t w,
     }
 }
 
-template <bool kVecH, bool kLdsW, bool kVecV>
+template <bool kVecH, bool kLdsW, bool kVecV, int kRootUnroll>
 __global__ __launch_bounds__(kFrontThreads) void step_front_kernel(FrontParams p) {
     extern __shared__ __align__(16) uint16_t dyn_lds[];
     __shared__ float z_s[DSPARK_MAX_GAMMA], p_s[DSPARK_MAX_GAMMA], s_s[DSPARK_MAX_GAMMA];
@@ -101,8 +109,9 @@ __global__ __launch_bounds__(kFrontThreads) void step_front_kernel(FrontParams p
     __shared__ int last_s;
     if ((int)blockIdx.x >= p.B) {
         const int nw = blockDim.x / kWave;
-        front_root_rows<kVecV>(p, (int64_t)((int)blockIdx.x - p.B) * nw + threadIdx.x / kWave,
-                               (int64_t)((int)gridDim.x - p.B) * nw);
+        front_root_rows<kVecV, kRootUnroll>(
+            p, (int64_t)((int)blockIdx.x - p.B) * nw + threadIdx.x / kWave,
+            (int64_t)((int)gridDim.x - p.B) * nw);
         return;
     }
     const int b = blockIdx.x;
@@ -333,16 +342,28 @@ static int stream_grid(size_t lds) {
     return gsz;
 }
 
+template <bool kVecV, int kRootUnroll>
+static void launch_front_u(bool hvec, bool ldsw, const FrontParams &fp, int root_wgs, size_t lds,
+                           hipStream_t s) {
+    const dim3 grid(fp.B + root_wgs), block(kFrontThreads);
+    if (hvec && ldsw)
+        hipLaunchKernelGGL((step_front_kernel<true, true, kVecV, kRootUnroll>), grid, block, lds, s,
+                           fp);
+    else if (hvec)
+        hipLaunchKernelGGL((step_front_kernel<true, false, kVecV, kRootUnroll>), grid, block, lds,
+                           s, fp);
+    else
+        hipLaunchKernelGGL((step_front_kernel<false, false, kVecV, kRootUnroll>), grid, block, lds,
+                           s, fp);
+}
+
 template <bool kVecV>
 static void launch_front(bool hvec, bool ldsw, const FrontParams &fp, int root_wgs, size_t lds,
                          hipStream_t s) {
-    const dim3 grid(fp.B + root_wgs), block(kFrontThreads);
-    if (hvec && ldsw)
-        hipLaunchKernelGGL((step_front_kernel<true, true, kVecV>), grid, block, lds, s, fp);
-    else if (hvec)
-        hipLaunchKernelGGL((step_front_kernel<true, false, kVecV>), grid, block, lds, s, fp);
+    if (fp.arrivals)
+        launch_front_u<kVecV, kRootUnrollWithPick>(hvec, ldsw, fp, root_wgs, lds, s);
     else
-        hipLaunchKernelGGL((step_front_kernel<false, false, kVecV>), grid, block, lds, s, fp);
+        launch_front_u<kVecV, kRootUnrollAlone>(hvec, ldsw, fp, root_wgs, lds, s);
 }
 
 hipError_t launch_fused_step(const uint16_t *hidden, const uint16_t *w, float bias,
