@@ -166,12 +166,26 @@ __global__ __launch_bounds__(kFrontThreads) void step_front_kernel(FrontParams p
     // combined cut: a position below its request's cutoff ranks below every
     // eligible one, and the budget is capped by the eligible count
     const bool combined = p.mode == DSPARK_CUT_COMBINED;
+    // N <= kFusedSelPer * blockDim: every load of a thread is issued before
+    // any is waited for (one round trip instead of kFusedSelPer)
+    float v[kFusedSelPer], c[kFusedSelPer];
+#pragma unroll
+    for (int j = 0; j < kFusedSelPer; ++j) {
+        const int f = tid + j * bd;
+        v[j] = f < N ? __hip_atomic_load(p.surv + f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                     : 0.0f;
+        c[j] = (combined && f < N) ? p.cutoff[f / p.gamma] : 0.0f;
+    }
     int n = 0;
-    for (int f = tid; f < N; f += bd) {
-        float v = __hip_atomic_load(p.surv + f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        if (combined && !(v >= p.cutoff[f / p.gamma])) v = -INFINITY;
-        else ++n;
-        sv[f] = v;
+#pragma unroll
+    for (int j = 0; j < kFusedSelPer; ++j) {
+        const int f = tid + j * bd;
+        if (f < N) {
+            float x = v[j];
+            if (combined && !(x >= c[j])) x = -INFINITY;
+            else ++n;
+            sv[f] = x;
+        }
     }
     int eligible;
     block_excl_scan(n, &eligible, scan_lds);  // contains the barriers sv needs
