@@ -14,11 +14,14 @@ namespace dspark {
 
 constexpr int kGemvUnroll = 4;  // 16-byte hidden loads in flight per lane
 
-// One wave per hidden row: z[i] = sum_k w[k]*h[b,i,k] + bias for the gamma rows
-// of one request. hidden_b points at row 0 of the request. kVec: d % 8 == 0
-// and both pointers 16-byte aligned, so each lane loads 8 bf16 per access.
-// w may live in LDS or global memory. The lane order of the fp32 accumulation
-// and the butterfly reduction are fixed, so results are bit-reproducible.
+// z[i] = sum_k w[k]*h[b,i,k] + bias for the gamma rows of one request, one
+// wave per row. hidden_b points at row 0 of the request. kVec: d % 8 == 0 and
+// both pointers 16-byte aligned, so each lane loads 8 bf16 per access. A wave
+// takes its rows two at a time (i and i + nwaves) and streams both together:
+// twice the hidden-state bytes in flight per wave, and each slice of w read
+// once for both rows. w may live in LDS or global memory. Each row's fp32
+// accumulation order (per lane, then the butterfly) is fixed and does not
+// depend on the pairing, so results are bit-reproducible.
 template <bool kVec>
 __device__ __forceinline__ void request_logits(const uint16_t *__restrict__ hidden_b,
                                                const uint16_t *__restrict__ w, float bias,
@@ -26,45 +29,64 @@ __device__ __forceinline__ void request_logits(const uint16_t *__restrict__ hidd
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = threadIdx.x / kWave;
     const int nwaves = blockDim.x / kWave;
-    for (int i = wave; i < gamma; i += nwaves) {
-        const uint16_t *h = hidden_b + (size_t)i * (size_t)d;
-        float acc = 0.0f;
+    for (int i0 = wave; i0 < gamma; i0 += 2 * nwaves) {
+        const int i1 = i0 + nwaves;
+        const bool two = i1 < gamma;
+        const uint16_t *h0 = hidden_b + (size_t)i0 * (size_t)d;
+        const uint16_t *h1 = hidden_b + (size_t)(two ? i1 : i0) * (size_t)d;
+        float acc0 = 0.0f, acc1 = 0.0f;
         if (kVec) {
-            const u32x4 *h4 = reinterpret_cast<const u32x4 *>(h);
+            const u32x4 *a4 = reinterpret_cast<const u32x4 *>(h0);
+            const u32x4 *b4 = reinterpret_cast<const u32x4 *>(h1);
             const u32x4 *w4 = reinterpret_cast<const u32x4 *>(w);
             const int nv = d >> 3;
             int v = lane;
-            // kGemvUnroll vectors per lane in flight per trip
             for (; v + (kGemvUnroll - 1) * kWave < nv; v += kGemvUnroll * kWave) {
-                u32x4 hv[kGemvUnroll], wv[kGemvUnroll];
+                u32x4 av[kGemvUnroll], bv[kGemvUnroll], wv[kGemvUnroll];
 #pragma unroll
                 for (int u = 0; u < kGemvUnroll; ++u) {
-                    hv[u] = __builtin_nontemporal_load(h4 + v + u * kWave);
+                    av[u] = __builtin_nontemporal_load(a4 + v + u * kWave);
+                    if (two) bv[u] = __builtin_nontemporal_load(b4 + v + u * kWave);
                     wv[u] = w4[v + u * kWave];
                 }
 #pragma unroll
                 for (int u = 0; u < kGemvUnroll; ++u) {
 #pragma unroll
                     for (int c = 0; c < 4; ++c) {
-                        acc = fmaf(bf16_lo(hv[u][c]), bf16_lo(wv[u][c]), acc);
-                        acc = fmaf(bf16_hi(hv[u][c]), bf16_hi(wv[u][c]), acc);
+                        acc0 = fmaf(bf16_lo(av[u][c]), bf16_lo(wv[u][c]), acc0);
+                        acc0 = fmaf(bf16_hi(av[u][c]), bf16_hi(wv[u][c]), acc0);
+                        if (two) {
+                            acc1 = fmaf(bf16_lo(bv[u][c]), bf16_lo(wv[u][c]), acc1);
+                            acc1 = fmaf(bf16_hi(bv[u][c]), bf16_hi(wv[u][c]), acc1);
+                        }
                     }
                 }
             }
             for (; v < nv; v += kWave) {
-                u32x4 hv = __builtin_nontemporal_load(h4 + v);
-                u32x4 wv = w4[v];
+                const u32x4 av = __builtin_nontemporal_load(a4 + v);
+                const u32x4 bv = two ? __builtin_nontemporal_load(b4 + v) : av;
+                const u32x4 wv = w4[v];
 #pragma unroll
                 for (int c = 0; c < 4; ++c) {
-                    acc = fmaf(bf16_lo(hv[c]), bf16_lo(wv[c]), acc);
-                    acc = fmaf(bf16_hi(hv[c]), bf16_hi(wv[c]), acc);
+                    acc0 = fmaf(bf16_lo(av[c]), bf16_lo(wv[c]), acc0);
+                    acc0 = fmaf(bf16_hi(av[c]), bf16_hi(wv[c]), acc0);
+                    acc1 = fmaf(bf16_lo(bv[c]), bf16_lo(wv[c]), acc1);
+                    acc1 = fmaf(bf16_hi(bv[c]), bf16_hi(wv[c]), acc1);
                 }
             }
         } else {
-            for (int k = lane; k < d; k += kWave) acc = fmaf(bf16_f32(h[k]), bf16_f32(w[k]), acc);
+            for (int k = lane; k < d; k += kWave) {
+                const float wk = bf16_f32(w[k]);
+                acc0 = fmaf(bf16_f32(h0[k]), wk, acc0);
+                acc1 = fmaf(bf16_f32(h1[k]), wk, acc1);
+            }
         }
-        acc = wave_sum_f32(acc);
-        if (lane == 0) z_lds[i] = acc + bias;
+        acc0 = wave_sum_f32(acc0);
+        acc1 = wave_sum_f32(acc1);
+        if (lane == 0) {
+            z_lds[i0] = acc0 + bias;
+            if (two) z_lds[i1] = acc1 + bias;
+        }
     }
 }
 

@@ -44,14 +44,15 @@ constexpr int kFrontRootWGsPerCU = 1;  // root-row workgroups of the front grid 
 constexpr int kStreamThreads = 512;
 constexpr int kStreamWavesPerCU = 16;  // target waves of the draft-row stream per CU
 constexpr int kStreamUnroll = 2;  // 16-byte loads in flight per lane (more waves, fewer bytes each)
-// Root rows of the front kernel: with no pick in the front (per-request cutoff,
-// static) the root rows are its critical path and get four loads in flight per
-// lane; when the front's last workgroup also runs the batch-wide pick, the
-// GEMV and pick chain is critical and the roots take two, leaving bandwidth to
-// the GEMV (measured: 110.5 against 113.4 us per step at the mixed workload's
-// threshold arm, 70.2 against 72.3 at its budget arm).
-constexpr int kRootUnrollAlone = 4;
-constexpr int kRootUnrollWithPick = 2;
+// Root rows of the front kernel: four 16-byte loads in flight per lane when
+// they are the front's critical path, two when the GEMV-and-pick chain is (the
+// last request workgroup runs the batch-wide pick after the slowest GEMV; a
+// request's GEMV reads gamma*d bf16, its root row V). Measured per step: the
+// mixed workload's threshold arm 111 us with four against 113-115 with two;
+// its budget arm (gamma*d = 65536 < V/2) 68.1 against 70.3; the budget
+// workload at d = 7168 (gamma*d = 114688 > V/2) 67.7 with two against 69.3.
+constexpr int kRootUnrollDeep = 4;
+constexpr int kRootUnrollShallow = 2;
 
 // ------------------------------------------------------------------ front
 
@@ -374,10 +375,12 @@ static void launch_front_u(bool hvec, bool ldsw, const FrontParams &fp, int root
 template <bool kVecV>
 static void launch_front(bool hvec, bool ldsw, const FrontParams &fp, int root_wgs, size_t lds,
                          hipStream_t s) {
-    if (fp.arrivals)
-        launch_front_u<kVecV, kRootUnrollWithPick>(hvec, ldsw, fp, root_wgs, lds, s);
+    const bool gemv_critical =
+        fp.arrivals != nullptr && (int64_t)fp.gamma * fp.d * 2 > (int64_t)fp.V;
+    if (gemv_critical)
+        launch_front_u<kVecV, kRootUnrollShallow>(hvec, ldsw, fp, root_wgs, lds, s);
     else
-        launch_front_u<kVecV, kRootUnrollAlone>(hvec, ldsw, fp, root_wgs, lds, s);
+        launch_front_u<kVecV, kRootUnrollDeep>(hvec, ldsw, fp, root_wgs, lds, s);
 }
 
 hipError_t launch_fused_step(const uint16_t *hidden, const uint16_t *w, float bias,
