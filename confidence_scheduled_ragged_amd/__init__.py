@@ -57,6 +57,7 @@ def lib() -> ctypes.CDLL:
         L.dspark_gather_rows.argtypes = [P, P, P, I, I, LL, P, P]
         L.dspark_tier_select.argtypes = [P, I, I, P, I, ctypes.c_int32, P, P, P, P, P]
         L.dspark_cost_cutoff.argtypes = [P, I, P, I, P, P]
+        L.dspark_step_profiled.argtypes = L.dspark_step.argtypes + [P, P]
         L.dspark_workspace_bytes.argtypes = [I, I, I]
         L.dspark_workspace_bytes.restype = S
         L.dspark_workspace_init.argtypes = [P, S, P]
@@ -64,7 +65,8 @@ def lib() -> ctypes.CDLL:
         L.dspark_status_string.restype = ctypes.c_char_p
         for f in (L.dspark_confidence, L.dspark_schedule, L.dspark_compact, L.dspark_accept,
                   L.dspark_step, L.dspark_workspace_init, L.dspark_cap_accept,
-                  L.dspark_gather_rows, L.dspark_tier_select, L.dspark_cost_cutoff):
+                  L.dspark_gather_rows, L.dspark_tier_select, L.dspark_cost_cutoff,
+                  L.dspark_step_profiled):
             f.restype = ctypes.c_int
         _lib = L
     return _lib
@@ -359,9 +361,22 @@ def alloc_step_outputs(B: int, gamma: int, device, with_conf: bool = True) -> Di
     return out
 
 
+def _event_handle(ev):
+    """Raw hipEvent_t of a torch.cuda.Event (created on first use) or a handle."""
+    if ev is None:
+        return None
+    if isinstance(ev, torch.cuda.Event):
+        if not ev.cuda_event:
+            ev.record()                  # torch creates the event lazily
+        return ctypes.c_void_p(ev.cuda_event)
+    return ctypes.c_void_p(int(ev))
+
+
 def dspark_step(hidden, w, bias, temps, tokens, logits, mode, cutoff=None, budget=0, out=None,
-                ws=None):
-    """Steps 1-6 in one call; returns the dict of output tensors."""
+                ws=None, events=None):
+    """Steps 1-6 in one call; returns the dict of output tensors. `events`, a
+    pair of timing events, selects dspark_step_profiled: they are recorded
+    around the step's dominant kernel."""
     B, g, d = hidden.shape
     V = logits.shape[-1]
     _need(hidden, "hidden", torch.bfloat16)
@@ -382,18 +397,32 @@ def dspark_step(hidden, w, bias, temps, tokens, logits, mode, cutoff=None, budge
         if out.get(k) is not None:
             _need(out[k], k, torch.float32 if k in ("conf", "survival") else torch.int32, shp)
     ws = workspace(B, g, V, dev) if ws is None else _need(ws, "ws", torch.uint8)
-    _ok("dspark_step", lib().dspark_step(
+    args = (
         _ptr(hidden), _ptr(w), float(bias), _ptr(temps), _ptr(tokens), _ptr(logits), B, g, d, V,
         m, _ptr(cutoff), int(budget), _ptr(out.get("conf")), _ptr(out.get("survival")),
         _ptr(out["lengths"]), _ptr(out["cu_seqlens"]), _ptr(out["packed_tokens"]),
         _ptr(out["packed_src_row"]), _ptr(out["packed_argmax"]), _ptr(out["accepted"]),
-        _ptr(out["bonus"]), _ptr(ws), ws.numel(), _stream(dev)))
+        _ptr(out["bonus"]), _ptr(ws), ws.numel(), _stream(dev))
+    if events is None:
+        _ok("dspark_step", lib().dspark_step(*args))
+    else:
+        _ok("dspark_step_profiled", lib().dspark_step_profiled(
+            *args, _event_handle(events[0]), _event_handle(events[1])))
     return out
+
+
+def dspark_step_profiled(hidden, w, bias, temps, tokens, logits, mode, events, cutoff=None,
+                         budget=0, out=None, ws=None):
+    """dspark_step with a pair of timing events recorded around its dominant
+    kernel (the draft-row stream)."""
+    return dspark_step(hidden, w, bias, temps, tokens, logits, mode, cutoff=cutoff,
+                       budget=budget, out=out, ws=ws, events=events)
 
 
 __all__ = ["DsparkError", "lib", "LIB_PATH", "dspark_status_string", "dspark_confidence", "dspark_schedule",
            "dspark_compact", "dspark_accept", "dspark_step", "dspark_cap_accept",
            "dspark_gather_rows", "dspark_tier_select", "dspark_cost_cutoff",
+           "dspark_step_profiled",
            "dspark_workspace_bytes",
            "dspark_workspace_init", "workspace", "alloc_step_outputs", "STEP_OUTPUTS",
            "DSPARK_CUT_THRESHOLD", "DSPARK_CUT_BUDGET", "DSPARK_CUT_STATIC",

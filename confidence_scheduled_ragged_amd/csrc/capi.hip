@@ -220,14 +220,15 @@ DSPARK_API dspark_status dspark_cap_accept(const int32_t *packed_argmax_full,
                                       bonus, accepted_full, sums, as_stream(stream)));
 }
 
-DSPARK_API dspark_status dspark_step(const dspark_bf16 *hidden, const dspark_bf16 *w, float bias,
+static dspark_status step_impl(const dspark_bf16 *hidden, const dspark_bf16 *w, float bias,
                                      const float *temps, const int32_t *tokens,
                                      const dspark_bf16 *logits, int B, int gamma, int d, int V,
                                      int mode, const float *cutoff, long long budget, float *conf,
                                      float *survival, int32_t *lengths, int32_t *cu_seqlens,
                                      int32_t *packed_tokens, int32_t *packed_src_row,
                                      int32_t *packed_argmax, int32_t *accepted, int32_t *bonus,
-                                     void *ws, size_t ws_bytes, void *stream) {
+                                     void *ws, size_t ws_bytes, void *stream, void *ev_start,
+                                     void *ev_stop) {
     if (!hidden || !w || !temps || !tokens || !logits || !lengths || !cu_seqlens ||
         !packed_tokens || !packed_src_row || !packed_argmax || !accepted || !bonus || !ws)
         return DSPARK_ERR_NULL;
@@ -249,17 +250,45 @@ DSPARK_API dspark_status dspark_step(const dspark_bf16 *hidden, const dspark_bf1
     char *wsb = static_cast<char *>(ws);
     float *surv = survival ? survival : reinterpret_cast<float *>(wsb + ws_surv_offset(B, gamma));
     float *cf = conf ? conf : reinterpret_cast<float *>(wsb + ws_conf_offset(B, gamma));
+    hipEvent_t es = static_cast<hipEvent_t>(ev_start), et = static_cast<hipEvent_t>(ev_stop);
     hipError_t e = launch_fused_step(hidden, w, bias, temps, tokens, logits, B, gamma, d, V, mode,
                                      cutoff, budget, cf, surv, lengths, cu_seqlens, packed_tokens,
-                                     packed_src_row, packed_argmax, accepted, bonus, ws, s);
+                                     packed_src_row, packed_argmax, accepted, bonus, ws, s, es, et);
     if (e != hipErrorNotSupported) return launched(e);
     // sizes outside the fused kernels' limits: the same step through the stage kernels
     e = launch_confidence(hidden, w, bias, temps, B, gamma, d, cf, surv, s);
     if (e == hipSuccess) e = launch_schedule(surv, B, gamma, mode, cutoff, budget, lengths, s);
     if (e == hipSuccess)
         e = launch_compact(lengths, tokens, B, gamma, cu_seqlens, packed_tokens, packed_src_row, s);
+    if (e == hipSuccess && es) e = hipEventRecord(es, s);
     if (e == hipSuccess)
         e = launch_accept(logits, packed_src_row, cu_seqlens, tokens, B, gamma, V, packed_argmax,
                           accepted, bonus, ws, s);
+    if (e == hipSuccess && et) e = hipEventRecord(et, s);
     return launched(e);
+}
+
+DSPARK_API dspark_status dspark_step(const dspark_bf16 *hidden, const dspark_bf16 *w, float bias,
+                                     const float *temps, const int32_t *tokens,
+                                     const dspark_bf16 *logits, int B, int gamma, int d, int V,
+                                     int mode, const float *cutoff, long long budget, float *conf,
+                                     float *survival, int32_t *lengths, int32_t *cu_seqlens,
+                                     int32_t *packed_tokens, int32_t *packed_src_row,
+                                     int32_t *packed_argmax, int32_t *accepted, int32_t *bonus,
+                                     void *ws, size_t ws_bytes, void *stream) {
+    return step_impl(hidden, w, bias, temps, tokens, logits, B, gamma, d, V, mode, cutoff, budget,
+                     conf, survival, lengths, cu_seqlens, packed_tokens, packed_src_row,
+                     packed_argmax, accepted, bonus, ws, ws_bytes, stream, nullptr, nullptr);
+}
+
+DSPARK_API dspark_status dspark_step_profiled(
+    const dspark_bf16 *hidden, const dspark_bf16 *w, float bias, const float *temps,
+    const int32_t *tokens, const dspark_bf16 *logits, int B, int gamma, int d, int V, int mode,
+    const float *cutoff, long long budget, float *conf, float *survival, int32_t *lengths,
+    int32_t *cu_seqlens, int32_t *packed_tokens, int32_t *packed_src_row, int32_t *packed_argmax,
+    int32_t *accepted, int32_t *bonus, void *ws, size_t ws_bytes, void *stream, void *ev_start,
+    void *ev_stop) {
+    return step_impl(hidden, w, bias, temps, tokens, logits, B, gamma, d, V, mode, cutoff, budget,
+                     conf, survival, lengths, cu_seqlens, packed_tokens, packed_src_row,
+                     packed_argmax, accepted, bonus, ws, ws_bytes, stream, ev_start, ev_stop);
 }

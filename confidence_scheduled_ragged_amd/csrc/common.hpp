@@ -155,6 +155,7 @@ hipError_t launch_fused_step(const uint16_t *hidden, const uint16_t *w, float bi
                              int B, int gamma, int d, int V, int mode, const float *cutoff,
                              long long budget, float *conf, float *surv, int32_t *lengths,
                              int32_t *cu, int32_t *ptok, int32_t *psrc, int32_t *pam,
-                             int32_t *acc, int32_t *bonus, void *ws, hipStream_t s);
+                             int32_t *acc, int32_t *bonus, void *ws, hipStream_t s,
+                             hipEvent_t ev_start = nullptr, hipEvent_t ev_stop = nullptr);
 
 }  // namespace dspark

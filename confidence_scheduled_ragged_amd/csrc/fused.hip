@@ -388,7 +388,8 @@ hipError_t launch_fused_step(const uint16_t *hidden, const uint16_t *w, float bi
                              int B, int gamma, int d, int V, int mode, const float *cutoff,
                              long long budget, float *conf, float *surv, int32_t *lengths,
                              int32_t *cu, int32_t *ptok, int32_t *psrc, int32_t *pam,
-                             int32_t *acc, int32_t *bonus, void *ws, hipStream_t s) {
+                             int32_t *acc, int32_t *bonus, void *ws, hipStream_t s,
+                             hipEvent_t ev_start, hipEvent_t ev_stop) {
     if (B > kMaxFusedB) return hipErrorNotSupported;
     char *wsb = static_cast<char *>(ws);
     uint64_t *keys = reinterpret_cast<uint64_t *>(wsb + ws_keys_offset());
@@ -474,11 +475,15 @@ hipError_t launch_fused_step(const uint16_t *hidden, const uint16_t *w, float bi
     if (max_wgs < stream_wgs_needed) stream_wgs_needed = max_wgs < 1 ? 1 : (int)max_wgs;
     int g = vvec ? stream_grid<true>(lds) : stream_grid<false>(lds);
     g = g < stream_wgs_needed ? g : stream_wgs_needed;
+    // measurement events bracket the dominant kernel (the draft-row stream)
+    if (ev_start && (e = hipEventRecord(ev_start, s)) != hipSuccess) return e;
     if (vvec)
         hipLaunchKernelGGL((step_stream_kernel<true>), dim3(g), dim3(kStreamThreads), lds, s, p);
     else
         hipLaunchKernelGGL((step_stream_kernel<false>), dim3(g), dim3(kStreamThreads), lds, s, p);
-    return hipGetLastError();
+    e = hipGetLastError();
+    if (e == hipSuccess && ev_stop) e = hipEventRecord(ev_stop, s);
+    return e;
 }
 
 }  // namespace dspark

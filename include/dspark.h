@@ -271,6 +271,25 @@ dspark_status dspark_step(const dspark_bf16 *hidden, const dspark_bf16 *w, float
                           int32_t *packed_argmax, int32_t *accepted, int32_t *bonus,
                           void *ws, size_t ws_bytes, void *stream);
 
+/*
+ * Measurement aid: dspark_step, plus hipEventRecord(ev_start, stream) right
+ * before the launch of the step's dominant kernel (the stream over the draft
+ * rows, which also writes the acceptance) and hipEventRecord(ev_stop, stream)
+ * right after it, so the elapsed time between the two events is that kernel's
+ * duration. ev_start / ev_stop are hipEvent_t handles (as void*) the caller
+ * created with timing enabled; either may be NULL. Results are identical to
+ * dspark_step's; nothing is allocated.
+ */
+dspark_status dspark_step_profiled(const dspark_bf16 *hidden, const dspark_bf16 *w, float bias,
+                                   const float *temps, const int32_t *tokens,
+                                   const dspark_bf16 *logits, int B, int gamma, int d, int V,
+                                   int mode, const float *cutoff, long long budget, float *conf,
+                                   float *survival, int32_t *lengths, int32_t *cu_seqlens,
+                                   int32_t *packed_tokens, int32_t *packed_src_row,
+                                   int32_t *packed_argmax, int32_t *accepted, int32_t *bonus,
+                                   void *ws, size_t ws_bytes, void *stream, void *ev_start,
+                                   void *ev_stop);
+
 /* Scratch bytes needed by dspark_accept and dspark_step for these sizes
  * (independent of d); 0 for invalid sizes. */
 size_t dspark_workspace_bytes(int B, int gamma, int V);

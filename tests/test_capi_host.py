@@ -162,6 +162,29 @@ def test_step_validation(L):
     assert step_call(L, wsb=100) == EWS
 
 
+def test_step_profiled_validation(L):
+    # the same checks as dspark_step (events are optional handles)
+    base = dict(hidden=A, w=A, bias=0.0, temps=A, tokens=A, logits=A, B=4, g=8, d=256, V=1024,
+                mode=0, cutoff=A, budget=0, conf=A, surv=A, lengths=A, cu=A, ptok=A, psrc=A,
+                pam=A, acc=A, bonus=A, ws=A, wsb=1 << 30)
+    f = lambda x: P(x) if x else None
+
+    def call(**kw):
+        a = dict(base)
+        a.update(kw)
+        return L.dspark_step_profiled(
+            f(a["hidden"]), f(a["w"]), a["bias"], f(a["temps"]), f(a["tokens"]), f(a["logits"]),
+            a["B"], a["g"], a["d"], a["V"], a["mode"], f(a["cutoff"]), a["budget"], f(a["conf"]),
+            f(a["surv"]), f(a["lengths"]), f(a["cu"]), f(a["ptok"]), f(a["psrc"]), f(a["pam"]),
+            f(a["acc"]), f(a["bonus"]), f(a["ws"]), a["wsb"], None, None, None)
+
+    assert call(logits=0) == ENULL
+    assert call(B=0) == ESHAPE
+    assert call(mode=9) == EARG
+    assert call(ws=A + 4) == EALIGN
+    assert call(wsb=100) == EWS
+
+
 def cap_call(L, pam=A, tok=A, lengths=A, B=4, g=8, acc=A, bon=A, full=A, sums=0):
     f = lambda x: P(x) if x else None
     return L.dspark_cap_accept(f(pam), f(tok), f(lengths), B, g, f(acc), f(bon), f(full),

@@ -107,3 +107,25 @@ def test_step_graph_replays_match_eager(name):
                     assert np.array_equal(got[k][:total], ev[:total]), (rep, i, k)
                 else:
                     assert np.array_equal(got[k], ev), (rep, i, k)
+
+
+@pytest.mark.parametrize("name", ["mixed_threshold", "mixed_budget"])
+def test_profiled_step_matches_step_and_brackets_the_dominant_kernel(name):
+    # dspark_step_profiled gives dspark_step's results and records its events
+    # around the stream kernel only: inside the step's own event pair
+    cfg = CONFIGS[name].scaled(B=128, V=65536)
+    s = make_step(cfg, 1, device=DEV)
+    ref = dspark.dspark_step(s.hidden, s.w, s.bias, s.temps, s.tokens, s.logits, cfg.mode,
+                             cutoff=s.cutoff, budget=s.budget)
+    ref = {k: v.cpu().numpy() for k, v in ref.items()}
+    e = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+    e[0].record()
+    got = dspark.dspark_step_profiled(s.hidden, s.w, s.bias, s.temps, s.tokens, s.logits,
+                                      cfg.mode, (e[1], e[2]), cutoff=s.cutoff, budget=s.budget)
+    e[3].record()
+    torch.cuda.synchronize()
+    for k, v in got.items():
+        assert np.array_equal(v.cpu().numpy(), ref[k]), k
+    step_ms, kern_ms = e[0].elapsed_time(e[3]), e[1].elapsed_time(e[2])
+    assert 0.0 < kern_ms < step_ms
+    assert e[0].elapsed_time(e[1]) > 0.0      # the front ran before the bracket opened
