@@ -156,7 +156,10 @@ DSPARK_API dspark_status dspark_gather_rows(const void *src, const int32_t *pack
                                             long long row_bytes, void *dst, void *stream) {
     if (!src || !packed_src_row || !cu_seqlens || !dst) return DSPARK_ERR_NULL;
     if (dspark_status st = check_bg(B, gamma)) return st;
-    if (row_bytes < 1 || row_bytes > ((long long)1 << 40)) return DSPARK_ERR_SHAPE;
+    // the source and destination each span B*(gamma+1) rows: keep their byte size
+    // within 2^48 so no offset computation can overflow
+    if (row_bytes < 1 || row_bytes > ((long long)1 << 48) / ((long long)B * (gamma + 1)))
+        return DSPARK_ERR_SHAPE;
     if (misaligned(packed_src_row, 4) || misaligned(cu_seqlens, 4)) return DSPARK_ERR_ALIGN;
     return launched(launch_gather_rows(src, packed_src_row, cu_seqlens, B, gamma,
                                        (int64_t)row_bytes, dst, as_stream(stream)));

@@ -27,8 +27,9 @@
  * ---------------------------------------
  * - Every array pointer is a DEVICE pointer to memory the caller allocated and
  *   owns. The library never allocates, frees or synchronises, keeps no state
- *   between calls (apart from a cached per-device compute-unit count) and
- *   does not retain any pointer after returning.
+ *   between calls (apart from cached per-device compute-unit counts and kernel
+ *   occupancy figures, filled on first use and safe to share between threads)
+ *   and does not retain any pointer after returning.
  * - Every call enqueues its kernels on `stream` (a hipStream_t passed as
  *   void*; NULL means the default stream) and returns without waiting. Results
  *   are ready when the stream reaches that point.
@@ -184,6 +185,7 @@ dspark_status dspark_tier_select(const int32_t *cu_seqlens, int B, int gamma,
  * and past cu_seqlens[B], and rows whose source index lies outside
  * [0, B*(gamma+1)), are left untouched. 16-byte accesses are used when
  * row_bytes and both pointers allow it, 4-byte or 1-byte otherwise.
+ * DSPARK_ERR_SHAPE when row_bytes < 1 or B*(gamma+1)*row_bytes exceeds 2^48.
  */
 dspark_status dspark_gather_rows(const void *src, const int32_t *packed_src_row,
                                  const int32_t *cu_seqlens, int B, int gamma, long long row_bytes,

@@ -213,6 +213,7 @@ def test_gather_rows_validation(L):
     assert gather_call(L, B=0) == ESHAPE
     assert gather_call(L, row_bytes=0) == ESHAPE
     assert gather_call(L, row_bytes=-8) == ESHAPE
+    assert gather_call(L, B=1 << 20, g=15, row_bytes=1 << 25) == ESHAPE   # 2^49 bytes
     assert gather_call(L, psrc=A + 2) == EALIGN
     assert gather_call(L, cu=A + 1) == EALIGN
 
