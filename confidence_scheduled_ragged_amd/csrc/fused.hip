@@ -105,7 +105,7 @@ template <bool kVecH, bool kLdsW, bool kVecV, int kRootUnroll>
 __global__ __launch_bounds__(kFrontThreads) void step_front_kernel(FrontParams p) {
     extern __shared__ __align__(16) uint16_t dyn_lds[];
     __shared__ float z_s[DSPARK_MAX_GAMMA], p_s[DSPARK_MAX_GAMMA], s_s[DSPARK_MAX_GAMMA];
-    __shared__ uint32_t hist[256], sh[2];
+    __shared__ uint32_t hist[4 * 256], sh[4];
     __shared__ int scan_lds[17];
     __shared__ int last_s;
     if ((int)blockIdx.x >= p.B) {
@@ -188,8 +188,11 @@ __global__ __launch_bounds__(kFrontThreads) void step_front_kernel(FrontParams p
             sv[f] = x;
         }
     }
-    int eligible;
-    block_excl_scan(n, &eligible, scan_lds);  // contains the barriers sv needs
+    int eligible = N;
+    if (combined)
+        block_excl_scan(n, &eligible, scan_lds);  // contains the barriers sv needs
+    else
+        __syncthreads();
     const int t = p.t < eligible ? p.t : eligible;
     if (t <= 0 || t >= N) {
         for (int r = tid; r < p.B; r += bd) p.lengths[r] = t <= 0 ? 0 : p.gamma;

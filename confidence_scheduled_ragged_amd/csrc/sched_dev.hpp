@@ -148,10 +148,13 @@ __device__ __forceinline__ BudgetCut budget_select(const float *__restrict__ sur
 // registers (N <= kPer * blockDim.x). Neighbouring positions of one request
 // have non-increasing survival, so their digits often repeat; equal digits of
 // consecutive positions are counted once per run, which keeps the LDS
-// histogram atomics off the few crowded bins.
+// histogram atomics off the few crowded bins. The four passes use four
+// histograms cleared up front, so a pass needs two barriers: after the
+// counts, and after the digit is chosen.
 template <int kPer>
 __device__ __forceinline__ BudgetCut budget_select_runs(const float *__restrict__ surv, int N, int t,
-                                                        uint32_t *hist /*256*/, uint32_t *sh /*2*/) {
+                                                        uint32_t *hist /*4*256*/,
+                                                        uint32_t *sh /*2*/) {
     const int tid = threadIdx.x;
     const int bd = blockDim.x;
     const int lane = tid & (kWave - 1);
@@ -166,11 +169,13 @@ __device__ __forceinline__ BudgetCut budget_select_runs(const float *__restrict_
         v[j] = ok ? ordered_f32(surv[f]) : 0u;
         nv += ok ? 1 : 0;
     }
+    for (int i = tid; i < 4 * 256; i += bd) hist[i] = 0;
+    __syncthreads();
     uint32_t prefix = 0, mask = 0;
     uint32_t remaining = (uint32_t)t;
-    for (int shift = 24; shift >= 0; shift -= 8) {
-        for (int i = tid; i < 256; i += bd) hist[i] = 0;
-        __syncthreads();
+    for (int pass = 0; pass < 4; ++pass) {
+        const int shift = 24 - 8 * pass;
+        uint32_t *h = hist + 256 * pass;
         uint32_t cur = 0xFFFFFFFFu, run = 0;
 #pragma unroll
         for (int j = 0; j < kPer; ++j) {
@@ -179,20 +184,20 @@ __device__ __forceinline__ BudgetCut budget_select_runs(const float *__restrict_
                 if (dg == cur) {
                     ++run;
                 } else {
-                    if (run) atomicAdd(&hist[cur], run);
+                    if (run) atomicAdd(&h[cur], run);
                     cur = dg;
                     run = 1;
                 }
             }
         }
-        if (run) atomicAdd(&hist[cur], run);
+        if (run) atomicAdd(&h[cur], run);
         __syncthreads();
         if (tid < kWave) {
             uint32_t c[4];
             uint32_t tot = 0;
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-                c[q] = hist[255 - 4 * lane - q];
+                c[q] = h[255 - 4 * lane - q];
                 tot += c[q];
             }
             const int inc = wave_incl_scan((int)tot, lane);
@@ -200,17 +205,18 @@ __device__ __forceinline__ BudgetCut budget_select_runs(const float *__restrict_
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
                 if (cum < remaining && remaining <= cum + c[q]) {
-                    sh[0] = prefix | ((uint32_t)(255 - 4 * lane - q) << shift);
-                    sh[1] = remaining - cum;
+                    sh[2 * (pass & 1)] = prefix | ((uint32_t)(255 - 4 * lane - q) << shift);
+                    sh[2 * (pass & 1) + 1] = remaining - cum;
                 }
                 cum += c[q];
             }
         }
         __syncthreads();
-        prefix = sh[0];
-        remaining = sh[1];
+        // the choice of this pass sits in its own pair of words, so the next
+        // pass may overwrite the other pair before every thread has read this one
+        prefix = sh[2 * (pass & 1)];
+        remaining = sh[2 * (pass & 1) + 1];
         mask |= 0xFFu << shift;
-        __syncthreads();
     }
     BudgetCut r;
     r.tau = prefix;
