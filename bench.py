@@ -542,6 +542,9 @@ def main():
     ap.add_argument("--rotation", type=int, default=8)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra-arms", action="store_true")
+    ap.add_argument("--profile-budget", action="store_true",
+                    help="time only the budget workload (d=7168 V=129280 T=768), for a kernel "
+                         "trace of that workload; prints its arm summary instead of the JSON line")
     ap.add_argument("--no-all-cores", action="store_true",
                     help="skip the oracle timing on all host cores")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -560,6 +563,15 @@ def main():
 
     dev = torch.device("cuda:0")
     dspark.lib()
+    if args.profile_budget:
+        cfg4 = CONFIGS["budget"]
+        p4 = make_params(cfg4)
+        slots4 = [make_step(cfg4, i, device=dev, params=p4) for i in range(args.rotation)]
+        outs4 = [dspark.alloc_step_outputs(cfg4.B, cfg4.gamma, dev) for _ in slots4]
+        ws4 = dspark.workspace(cfg4.B, cfg4.gamma, cfg4.V, dev)
+        r_4 = run_arm(cfg4, slots4, outs4, ws4, args.steps, args.warmup, dspark, torch)
+        print(json.dumps(arm_summary(cfg4, r_4, args.steps, cfg4.B)), flush=True)
+        return
     cfg_t = CONFIGS["mixed_threshold"]
     cfg_b = CONFIGS["mixed_budget"]
     params = make_params(cfg_t)
@@ -692,6 +704,8 @@ def main():
                      "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": k_gbs / HBM_PEAK_GBS,
                      "traffic": traffic["stream_kernel"] if traffic else None,
+                     "traffic_over_algorithmic": (traffic["stream_kernel"] / r_k["kernel_bytes"]
+                                                  if traffic else None),
                      "algorithmic_bytes_per_launch": r_k["kernel_bytes"],
                      "mean_launch_us": r_k["kernel_mean_ms"] * 1e3,
                      "timing": "second pass of the same steps through dspark_step_profiled"},
@@ -702,6 +716,8 @@ def main():
                           "peak": HBM_PEAK_GBS, "unit": "GB/s",
                           "frac": mean_bytes / (r_t["mean_step_ms"] / 1e3) / 1e9 / HBM_PEAK_GBS,
                           "traffic": traffic["step"] if traffic else None,
+                          "traffic_over_algorithmic": (traffic["step"] / mean_bytes
+                                                       if traffic else None),
                           "algorithmic_bytes_per_launch": mean_bytes,
                           "mean_launch_us": r_t["mean_step_ms"] * 1e3},
         "cpu_baseline": cpu,
