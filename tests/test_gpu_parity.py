@@ -276,8 +276,8 @@ def test_step_mixed_workload(name):
 
 
 @pytest.mark.parametrize("case", ["gamma1", "all_zero", "all_full", "budget0", "budget_all",
-                                  "nan_cut", "odd_vocab", "tiny_vocab", "big_gamma",
-                                  "stage_path_budget", "stage_path_wide"])
+                                  "nan_cut", "odd_vocab", "tiny_vocab", "big_gamma", "max_gamma",
+                                  "max_gamma_budget", "stage_path_budget", "stage_path_wide"])
 def test_step_edge_cases(case):
     base = CONFIGS["tiny"]
     cfg = {
@@ -290,6 +290,9 @@ def test_step_edge_cases(case):
         "odd_vocab": base.scaled(V=1001, d=250),
         "tiny_vocab": base.scaled(V=3, B=7),
         "big_gamma": base.scaled(gamma=64, B=3, V=4096),
+        # the largest drafted block the ABI takes (gamma = 256)
+        "max_gamma": base.scaled(gamma=256, B=2, V=512, d=64),
+        "max_gamma_budget": CONFIGS["mixed_budget"].scaled(gamma=256, B=12, V=512, d=64),
         # beyond the fused kernels' limits (B*gamma > 8192 in budget mode, B > 4096):
         # dspark_step runs the stage kernels
         "stage_path_budget": CONFIGS["mixed_budget"].scaled(B=600, d=256, V=512),

@@ -43,9 +43,12 @@ def _oracle_full_argmax(s):
     return oracle.argmax_rows(s.host_rows(np.arange(B * g1, dtype=np.int32)))
 
 
-@pytest.mark.parametrize("name,steps", [("tiny", 3), ("mid", 2), ("mixed_threshold", 1)])
+@pytest.mark.parametrize("name,steps", [("tiny", 3), ("mid", 2), ("mixed_threshold", 1),
+                                        ("stage_path", 1)])
 def test_static_step_matches_oracle(name, steps):
-    cfg = CONFIGS[name]
+    # "stage_path": B > 4096 takes the stage kernels inside dspark_step
+    cfg = (CONFIGS["tiny"].scaled(B=4200, gamma=2, d=64, V=64) if name == "stage_path"
+           else CONFIGS[name])
     for step in range(steps):
         s = make_step(cfg, step, device=DEV)
         g = {k: host(v) for k, v in _static_step(s).items()}
