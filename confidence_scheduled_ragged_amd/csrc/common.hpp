@@ -96,6 +96,9 @@ __device__ __forceinline__ int64_t sub_len(int64_t E, int64_t Wt) {
 //                                large enough for
 // rcnt:  uint64 [kMaxFusedB]     per-request arrival counters of the fused
 //                                step's stream kernel (zeroed by its front)
+// acnt:  uint64 [kMaxFusedB]     per-request arrival counters of dspark_accept
+//                                (zero between calls: each request's last
+//                                arriver resets its own)
 // keys:  uint64 [kMaxWaves + B*(gamma+1)] argmax segment keys of packed rows
 // rkeys: uint64 [kMaxWaves + B]  segment keys of the root rows (fused step)
 // surv:  float [B*gamma]         survival scratch (when the caller passes none)
@@ -106,7 +109,8 @@ constexpr size_t kCtrlBytes = 256;
 
 inline size_t ws_ctrl_offset() { return 0; }
 inline size_t ws_rcnt_offset() { return kCtrlBytes; }
-inline size_t ws_keys_offset() { return kCtrlBytes + (size_t)8 * kMaxFusedB; }
+inline size_t ws_acnt_offset() { return kCtrlBytes + (size_t)8 * kMaxFusedB; }
+inline size_t ws_keys_offset() { return kCtrlBytes + (size_t)16 * kMaxFusedB; }
 inline size_t ws_rkeys_offset(int64_t B, int64_t gamma) {
     return ws_keys_offset() + (size_t)8 * (size_t)(kMaxWaves + B * (gamma + 1));
 }
