@@ -322,3 +322,28 @@ def test_step_leaves_packed_tails_untouched():
     for k in ("packed_tokens", "packed_src_row", "packed_argmax"):
         assert np.all(g[k][total:] == -7)
         assert np.all(g[k][:total] != -7)
+
+
+def test_accept_malformed_offsets_leave_the_next_call_correct():
+    # cu_seqlens out of order and past the capacity: the outputs are
+    # unspecified but every access stays in bounds, and the per-request counters
+    # the call used return to zero, so a well-formed call on the same workspace
+    # right after it matches the oracle.
+    B, g, V = 6, 3, 512
+    L, tok, bits, cu, ps = _accept_case(B, g, V, seed=77)
+    lg = bits_tensor(bits)
+    ws = dspark.workspace(B, g, V, DEV)
+    bad_cu = torch.tensor([0, 9, 4, 30, 2, 12, 7], dtype=torch.int32, device=DEV)
+    bad_src = torch.tensor(np.arange(B * (g + 1)) % (B * (g + 1)), dtype=torch.int32,
+                           device=DEV)
+    dspark.dspark_accept(lg, bad_src, bad_cu, torch.from_numpy(tok).to(DEV), ws=ws)
+    torch.cuda.synchronize()
+    total = int(cu[-1])
+    pam, acc, bon = dspark.dspark_accept(lg, torch.from_numpy(ps).to(DEV),
+                                         torch.from_numpy(cu).to(DEV),
+                                         torch.from_numpy(tok).to(DEV), ws=ws)
+    torch.cuda.synchronize()
+    amax = oracle.argmax_rows(bits.reshape(-1, V), ps[:total])
+    o_acc, o_bon = oracle.accept(cu, tok, amax)
+    assert np.array_equal(host(pam)[:total], amax)
+    assert np.array_equal(host(acc), o_acc) and np.array_equal(host(bon), o_bon)
