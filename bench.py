@@ -17,10 +17,11 @@ step. One JSON line goes to stdout; progress goes to stderr.
 Reported:
   value        packed verify rows per second (sum of cu_seqlens[B] over the
                K steps / elapsed time)
-  roofline     the dominant kernel (step_stream_kernel): its algorithmic bytes
-               per launch / its mean duration between HIP events recorded
-               around its launch, against the 8 TB/s HBM peak
-  step_roofline the same for the whole step (both kernels)
+  roofline     the dominant kernel: its algorithmic bytes per launch / its
+               mean duration between HIP events recorded around its launch,
+               against the 8 TB/s HBM peak. With a per-request cutoff the step
+               is one launch (step_one_kernel), so that kernel is the step.
+  step_roofline the same for the whole step, events around the call
   cpu_baseline the fp64 oracle's whole step on the host (one thread) on a
                bounded sample of the same batches, in the same unit
 """
@@ -67,7 +68,7 @@ def recorded_traffic():
         return None
     try:
         return dict(step=float(kv["hbm_bytes_per_step"]),
-                    stream_kernel=float(kv["hbm_bytes_stream_kernel"]))
+                    kernel=float(kv["hbm_bytes_dominant_kernel"]))
     except (KeyError, ValueError):
         return None
 
@@ -92,11 +93,15 @@ def step_bytes(cfg, total: int) -> int:
     return reads + writes
 
 
-def stream_kernel_bytes(cfg, total: int) -> int:
-    """Algorithmic HBM bytes of the step's dominant kernel (step_stream_kernel):
-    the draft rows (packed rows other than the roots, which the front reads),
-    the lengths and verify-block tokens it reads, and every output it writes
+def dominant_kernel_bytes(cfg, total: int) -> int:
+    """Algorithmic HBM bytes of the step's dominant kernel. Threshold and static
+    cuts run the step in one launch: all of step_bytes. Budget and combined cuts
+    take two, and the second (step_stream_kernel) dominates: the draft rows
+    (packed rows other than the roots, which the first launch reads), the
+    lengths and verify-block tokens it reads, and every output it writes
     (cu_seqlens, packed tokens / source rows / argmax, accepted, bonus)."""
+    if cfg.mode in ("threshold", "static"):
+        return step_bytes(cfg, total)
     B, g, V = cfg.B, cfg.gamma, cfg.V
     reads = 2 * V * (total - B) + 4 * B + 4 * B * (g + 1)
     writes = 4 * (B + 1) + 12 * total + 8 * B
@@ -163,7 +168,7 @@ def run_arm(cfg, slots, outs, ws, steps, warmup, dspark, torch, kernel_events=Fa
                step_ms_sorted=sorted(step_ms), totals=totals)
     if kernel_ms:
         res["kernel_mean_ms"] = sum(kernel_ms) / steps
-        res["kernel_bytes"] = sum(stream_kernel_bytes(cfg, totals[i % R])
+        res["kernel_bytes"] = sum(dominant_kernel_bytes(cfg, totals[i % R])
                                   for i in range(steps)) / steps
     return res
 
@@ -697,21 +702,22 @@ def main():
                     "p10": s_t["p10_ms"] * 1e3, "p50": s_t["p50_ms"] * 1e3,
                     "p90": s_t["p90_ms"] * 1e3},
         "roofline": {"bound": "hbm",
-                     "kernel": "step_stream_kernel (draft-row argmax, compaction outputs, "
-                               "acceptance, bonus), timed live between HIP events recorded "
-                               "around its launch by dspark_step_profiled",
+                     "kernel": "step_one_kernel (the whole step in one launch: confidence "
+                               "GEMV, survival, cut, compaction outputs, root and draft-row "
+                               "argmax, acceptance, bonus), timed live between HIP events "
+                               "recorded around its launch by dspark_step_profiled",
                      "achieved": k_gbs,
                      "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": k_gbs / HBM_PEAK_GBS,
-                     "traffic": traffic["stream_kernel"] if traffic else None,
-                     "traffic_over_algorithmic": (traffic["stream_kernel"] / r_k["kernel_bytes"]
+                     "traffic": traffic["kernel"] if traffic else None,
+                     "traffic_over_algorithmic": (traffic["kernel"] / r_k["kernel_bytes"]
                                                   if traffic else None),
                      "algorithmic_bytes_per_launch": r_k["kernel_bytes"],
                      "mean_launch_us": r_k["kernel_mean_ms"] * 1e3,
                      "timing": "second pass of the same steps through dspark_step_profiled"},
         "step_roofline": {"bound": "hbm",
-                          "kernel": "the whole dspark_step: step_front_kernel + "
-                                    "step_stream_kernel (one stream), events around the call",
+                          "kernel": "the whole dspark_step (one launch), events around the "
+                                    "call",
                           "achieved": mean_bytes / (r_t["mean_step_ms"] / 1e3) / 1e9,
                           "peak": HBM_PEAK_GBS, "unit": "GB/s",
                           "frac": mean_bytes / (r_t["mean_step_ms"] / 1e3) / 1e9 / HBM_PEAK_GBS,

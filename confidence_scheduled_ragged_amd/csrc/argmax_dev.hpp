@@ -114,27 +114,33 @@ __device__ __forceinline__ uint64_t load_key_coherent(const uint64_t *p) {
     return __hip_atomic_load(const_cast<uint64_t *>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Argmax of packed row r from the keys of the waves whose shares touch it.
-// kCoherent: the keys were written by this same kernel. The key loads are
-// issued four at a time, so a row costs one memory round trip in the usual
-// case of at most four segments.
+// Index of the largest key among keys[s + r] for s in [s_lo, s_hi]: the
+// segment keys of row r left by sub-chunks s_lo..s_hi. kCoherent: the keys were
+// written by this same kernel. The loads are issued four at a time, so a row
+// costs one memory round trip in the usual case of at most four segments.
 template <bool kCoherent = false>
-__device__ __forceinline__ int32_t row_argmax(const uint64_t *__restrict__ keys, int64_t r,
-                                              int64_t Vv, int64_t Q) {
-    const int64_t w_lo = (r * Vv) / Q;
-    const int64_t w_hi = ((r + 1) * Vv - 1) / Q;
+__device__ __forceinline__ int32_t segment_keys_argmax(const uint64_t *__restrict__ keys, int64_t r,
+                                                       int64_t s_lo, int64_t s_hi) {
     uint64_t k = 0;
-    for (int64_t w = w_lo; w <= w_hi; w += 4) {
+    for (int64_t w = s_lo; w <= s_hi; w += 4) {
         uint64_t x[4];
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
-            const int64_t i = w + u <= w_hi ? w + u + r : w_lo + r;  // in range, repeats are harmless
+            const int64_t i = w + u <= s_hi ? w + u + r : s_lo + r;  // in range, repeats are harmless
             x[u] = kCoherent ? load_key_coherent(keys + i) : keys[i];
         }
 #pragma unroll
         for (int u = 0; u < 4; ++u) k = x[u] > k ? x[u] : k;
     }
     return key_index(k);
+}
+
+// Argmax of packed row r from the keys of the waves whose shares (Q slots
+// each, Vv slots per row) touch it.
+template <bool kCoherent = false>
+__device__ __forceinline__ int32_t row_argmax(const uint64_t *__restrict__ keys, int64_t r,
+                                              int64_t Vv, int64_t Q) {
+    return segment_keys_argmax<kCoherent>(keys, r, (r * Vv) / Q, ((r + 1) * Vv - 1) / Q);
 }
 
 // Acceptance and bonus of one request by one wave, from its verified rows'

@@ -89,13 +89,14 @@ __device__ __forceinline__ int64_t sub_len(int64_t E, int64_t Wt) {
 }
 
 // ------------------------------------------------------------ workspace map
-// ctrl:  [0, 256)                arrival counter of the fused step's front
-//                                workgroups (uint32 at offset 0); zero between
+// ctrl:  [0, 256)                control words of the fused step (arrival
+//                                counters and flags, below); zero between
 //                                calls, at the same place for every size, so
 //                                one workspace serves calls of any size it is
 //                                large enough for
 // rcnt:  uint64 [kMaxFusedB]     per-request arrival counters of the fused
-//                                step's stream kernel (zeroed by its front)
+//                                step (zero between calls: each request's last
+//                                arriver resets its own)
 // acnt:  uint64 [kMaxFusedB]     per-request arrival counters of dspark_accept
 //                                (zero between calls: each request's last
 //                                arriver resets its own)
@@ -106,6 +107,12 @@ __device__ __forceinline__ int64_t sub_len(int64_t E, int64_t Wt) {
 constexpr int64_t kMaxWaves = 16384;  // bound on waves (or sub-chunks) per pass
 constexpr int kMaxFusedB = 4096;      // largest batch of the fused step
 constexpr size_t kCtrlBytes = 256;
+// Words of the ctrl region: at 0 the arrival counter of the request
+// workgroups (both forms of the fused step); on the next 128-byte line the
+// one-launch step's count of workgroups yet to leave once the lengths are
+// final, and its time-out flag. The counters are zero between calls.
+constexpr size_t kCtrlGoOffset = 128;
+constexpr size_t kCtrlTimedOutOffset = 192;
 
 inline size_t ws_ctrl_offset() { return 0; }
 inline size_t ws_rcnt_offset() { return kCtrlBytes; }

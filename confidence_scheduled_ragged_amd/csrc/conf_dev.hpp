@@ -22,7 +22,9 @@ constexpr int kGemvUnroll = 4;  // 16-byte hidden loads in flight per lane
 // once for both rows. w may live in LDS or global memory. Each row's fp32
 // accumulation order (per lane, then the butterfly) is fixed and does not
 // depend on the pairing, so results are bit-reproducible.
-template <bool kVec>
+// kUnroll: 16-byte hidden loads in flight per lane and row; each lane still
+// accumulates its slots in increasing order, whatever the unrolling.
+template <bool kVec, int kUnroll = kGemvUnroll>
 __device__ __forceinline__ void request_logits(const uint16_t *__restrict__ hidden_b,
                                                const uint16_t *__restrict__ w, float bias,
                                                int gamma, int d, float *z_lds) {
@@ -41,16 +43,16 @@ __device__ __forceinline__ void request_logits(const uint16_t *__restrict__ hidd
             const u32x4 *w4 = reinterpret_cast<const u32x4 *>(w);
             const int nv = d >> 3;
             int v = lane;
-            for (; v + (kGemvUnroll - 1) * kWave < nv; v += kGemvUnroll * kWave) {
-                u32x4 av[kGemvUnroll], bv[kGemvUnroll], wv[kGemvUnroll];
+            for (; v + (kUnroll - 1) * kWave < nv; v += kUnroll * kWave) {
+                u32x4 av[kUnroll], bv[kUnroll], wv[kUnroll];
 #pragma unroll
-                for (int u = 0; u < kGemvUnroll; ++u) {
+                for (int u = 0; u < kUnroll; ++u) {
                     av[u] = __builtin_nontemporal_load(a4 + v + u * kWave);
                     if (two) bv[u] = __builtin_nontemporal_load(b4 + v + u * kWave);
                     wv[u] = w4[v + u * kWave];
                 }
 #pragma unroll
-                for (int u = 0; u < kGemvUnroll; ++u) {
+                for (int u = 0; u < kUnroll; ++u) {
 #pragma unroll
                     for (int c = 0; c < 4; ++c) {
                         acc0 = fmaf(bf16_lo(av[u][c]), bf16_lo(wv[u][c]), acc0);

@@ -1,27 +1,35 @@
-// fused.hip - the whole verify step as two launches on one stream.
+// fused.hip - the whole verify step on one stream, in one launch (threshold
+// and static cuts) or two (budget and combined cuts, whose batch-wide pick
+// must see every request's survival).
 //
-//   front   two kinds of workgroup in one grid. Workgroup b < B: the confidence
-//           GEMV of request b's gamma hidden rows, the STS sigmoid, the
-//           sequential survival product and, in threshold mode, the verify
-//           length. The other workgroups stream the root rows (row 0 of every
-//           request, verified whatever the cut) while the GEMV runs, and leave
-//           argmax keys of their segments. In budget mode the last request
-//           workgroup to finish (counted on an atomic arrival counter, no
-//           waiting) runs the batch-wide top-T pick and writes every length.
-//   stream  every workgroup scans the verify lengths into cu_seqlens in LDS and
-//           writes the schedule outputs of its own requests; then the draft
-//           rows of all requests, laid end to end, are cut into sub-chunks of
-//           about equal length, one contiguous run per wave, and each wave
-//           leaves one argmax key per row segment. A per-request atomic counts
-//           the draft slots done; the wave that completes a request merges its
-//           keys and writes the acceptance and bonus token (no waiting).
+// One launch: a grid of request workgroups (the confidence GEMV of their
+// requests' gamma hidden rows, the STS sigmoid, the sequential survival
+// product and the verify length), root workgroups (the root rows, verified
+// whatever the cut, streamed while the GEMV runs) and plain stream
+// workgroups. The last request workgroup to finish (an atomic arrival count)
+// raises a flag; every workgroup waits for it once, scans the lengths into
+// cu_seqlens in LDS, writes the schedule outputs of its own requests and
+// streams one contiguous sub-chunk of the draft rows. Root-row waves reach
+// the drafts later and get shorter sub-chunks. Per-request atomics count the
+// streamed slots of the root row and the drafts; the wave that completes a
+// request merges its keys and writes the acceptance and bonus token.
+//
+// Two launches:
+//   front   request workgroups as above and root workgroups; in budget mode
+//           the last request workgroup to finish (counted, no waiting) runs
+//           the batch-wide top-T pick and writes every length.
+//   stream  every workgroup scans the lengths and writes its schedule
+//           outputs; the draft rows are cut into sub-chunks of about equal
+//           length, one contiguous run per wave, and the wave that completes
+//           a request's draft rows finishes it.
 //
 // Long contiguous runs per wave were measured faster than small interleaved
 // sub-chunks (HBM row-buffer locality), and two 16-byte loads in flight per
 // lane with full occupancy faster than deeper unrolling with fewer waves.
 // Dynamic hand-out through per-XCD atomic work queues was measured slower:
-// one queue address serves about one ticket per 11-15 ns. Grid-wide waits
-// were measured at 16-76 us each and are not used.
+// one queue address serves about one ticket per 11-15 ns. Grid-wide barriers
+// were measured at 16-76 us each and are not used; the one-launch form's
+// single wait is one-directional (workgroups that never wait raise the flag).
 //
 // [P1] "DFlash to DSpark in SGLang", sections "DSpark: a sequential head and a
 // verify budget" (head, survival, cut), "Ragged verify under full CUDA graphs"
@@ -29,6 +37,7 @@
 // (the schedule and packing fused around the verify) and "Background"
 // (greedy acceptance and bonus token).
 #include <atomic>
+#include <cstdlib>
 
 #include "argmax_dev.hpp"
 #include "conf_dev.hpp"
@@ -52,6 +61,15 @@ constexpr int kStreamUnroll = 2;  // 16-byte loads in flight per lane (more wave
 // its budget arm (gamma*d = 65536 < V/2) 68.1 against 70.3; the budget
 // workload at d = 7168 (gamma*d = 114688 > V/2) 67.7 with two against 69.3.
 constexpr int kRootUnrollDeep = 4;
+// The one-launch step: 16-byte loads in flight per lane in the GEMV, the root
+// rows and the draft rows (its grid holds four waves per SIMD, so deeper
+// unrolling costs no occupancy), and the extra draft slots per early wave, as
+// a fraction of a root wave's root-row slots: about the root work left when
+// the lengths come out.
+constexpr int kOneGemvUnroll = 4;
+constexpr int kOneRootUnroll = 4;
+constexpr int kOneStreamUnroll = 2;
+constexpr double kLead = 0.45;
 constexpr int kRootUnrollShallow = 2;
 
 // ------------------------------------------------------------------ front
@@ -72,8 +90,9 @@ struct FrontParams {
 // Root rows (dense row b*(gamma+1) of every request b), laid end to end and
 // cut into sub-chunks of about equal length, one per root wave: wave w of
 // nwaves streams sub-chunks w, w + nwaves, ... and leaves one key per row
-// segment at rkeys[s + b].
-template <bool kVec, int kRootUnroll>
+// segment at rkeys[s + b]. kCoherent: the keys are read by other workgroups of
+// the same grid.
+template <bool kVec, int kRootUnroll, bool kCoherent>
 __device__ __forceinline__ void front_root_rows(const FrontParams &p, int64_t w, int64_t nwaves) {
     const int lane = threadIdx.x & (kWave - 1);
     const int64_t Vv = kVec ? (p.V >> 3) : p.V;
@@ -94,76 +113,77 @@ __device__ __forceinline__ void front_root_rows(const FrontParams &p, int64_t w,
                                                   seg_end - r * Vv, lane, best, bidx);
             uint64_t key = bidx >= 0 ? argmax_key(best, (uint32_t)bidx) : 0ull;
             key = wave_max_u64(key);
-            if (lane == 0) p.rkeys[cur + r] = key;
+            if (lane == 0) {
+                if (kCoherent)
+                    store_key_coherent(p.rkeys + cur + r, key);
+                else
+                    p.rkeys[cur + r] = key;
+            }
             e = seg_end;
             ++r;
         }
     }
 }
 
-template <bool kVecH, bool kLdsW, bool kVecV, int kRootUnroll>
-__global__ __launch_bounds__(kFrontThreads) void step_front_kernel(FrontParams p) {
-    extern __shared__ __align__(16) uint16_t dyn_lds[];
-    __shared__ float z_s[DSPARK_MAX_GAMMA], p_s[DSPARK_MAX_GAMMA], s_s[DSPARK_MAX_GAMMA];
-    __shared__ uint32_t hist[4 * 256], sh[4];
-    __shared__ int scan_lds[17];
-    __shared__ int last_s;
-    if ((int)blockIdx.x >= p.B) {
-        const int nw = blockDim.x / kWave;
-        front_root_rows<kVecV, kRootUnroll>(
-            p, (int64_t)((int)blockIdx.x - p.B) * nw + threadIdx.x / kWave,
-            (int64_t)((int)gridDim.x - p.B) * nw);
-        return;
+// The row segments of root wave w's sub-chunks (as front_root_rows cuts them):
+// f(b, n) for each, n slots of request b's root row.
+template <typename F>
+__device__ __forceinline__ void root_segments(int64_t E, int64_t K, int64_t Vv, int64_t w,
+                                              int64_t nwaves, F f) {
+    const int64_t NS = (E + K - 1) / K;
+    for (int64_t cur = w; cur < NS; cur += nwaves) {
+        int64_t e = cur * K;
+        const int64_t e_end = e + K < E ? e + K : E;
+        int64_t r = e / Vv;
+        while (e < e_end) {
+            const int64_t row_end = (r + 1) * Vv;
+            const int64_t seg_end = e_end < row_end ? e_end : row_end;
+            f((int)r, seg_end - e);
+            e = seg_end;
+            ++r;
+        }
     }
-    const int b = blockIdx.x;
+}
+
+// Confidence scores, survival curve and (threshold, static) verify length of
+// request b by the whole workgroup; w_s is the head (LDS or global).
+// coherent_surv / coherent_len: survival / the length are read by other
+// workgroups of the same grid, so they are written through to the device
+// coherence point.
+template <bool kVecH, int kGemvU = kGemvUnroll>
+__device__ __forceinline__ void front_request(const FrontParams &p, const uint16_t *w_s, int b,
+                                              bool coherent_surv, bool coherent_len, float *z_s,
+                                              float *p_s, float *s_s) {
     const int tid = threadIdx.x, bd = blockDim.x;
-    if (tid == 0)
-        __hip_atomic_store(p.req_arrivals + b, (uint64_t)0, __ATOMIC_RELAXED,
-                           __HIP_MEMORY_SCOPE_AGENT);
-    const uint16_t *wp = p.w;
-    if (kLdsW) {
-        stage_w(p.w, p.d, dyn_lds);
-        __syncthreads();
-        wp = dyn_lds;
-    }
-    request_logits<kVecH>(p.hidden + (size_t)b * p.gamma * p.d, wp, p.bias, p.gamma, p.d, z_s);
+    request_logits<kVecH, kGemvU>(p.hidden + (size_t)b * p.gamma * p.d, w_s, p.bias, p.gamma, p.d,
+                                  z_s);
     __syncthreads();
     request_survival(z_s, p.temps, p.gamma, p_s, s_s, p.conf + (size_t)b * p.gamma, nullptr);
-    const bool select_here = p.arrivals != nullptr;
     float *surv_b = p.surv + (size_t)b * p.gamma;
     for (int i = tid; i < p.gamma; i += bd) {
-        // the select reads survival from another workgroup of this grid: write
-        // it through to the device coherence point
-        if (select_here)
+        if (coherent_surv)
             __hip_atomic_store(surv_b + i, s_s[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         else
             surv_b[i] = s_s[i];
     }
-    if (p.mode == DSPARK_CUT_THRESHOLD) {
-        if (tid == 0) p.lengths[b] = threshold_length(s_s, p.gamma, p.cutoff[b]);
-        return;
+    if (tid == 0 && (p.mode == DSPARK_CUT_THRESHOLD || p.mode == DSPARK_CUT_STATIC)) {
+        const int L = p.mode == DSPARK_CUT_THRESHOLD ? threshold_length(s_s, p.gamma, p.cutoff[b])
+                                                     : p.gamma;
+        if (coherent_len)
+            __hip_atomic_store(p.lengths + b, L, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        else
+            p.lengths[b] = L;
     }
-    if (p.mode == DSPARK_CUT_STATIC) {
-        if (tid == 0) p.lengths[b] = p.gamma;
-        return;
-    }
-    if (!select_here) return;
+}
 
-    // budget: count this request as done once its survival stores are complete;
-    // the workgroup that counts the last request picks for the whole batch
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    if (tid == 0) {
-        const unsigned old = __hip_atomic_fetch_add(p.arrivals, 1u, __ATOMIC_RELAXED,
-                                                    __HIP_MEMORY_SCOPE_AGENT);
-        last_s = old == (unsigned)(p.B - 1);
-    }
-    __syncthreads();
-    if (!last_s) return;
-    if (tid == 0) __hip_atomic_store(p.arrivals, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+// Budget / combined: the batch-wide pick over every request's survival (read
+// from the device coherence point: other workgroups wrote it) by one
+// workgroup; writes every length. sv: LDS for N = B*gamma floats.
+__device__ __forceinline__ void front_pick(const FrontParams &p, float *sv, uint32_t *hist,
+                                           uint32_t *sh, int *scan_lds) {
+    const int tid = threadIdx.x, bd = blockDim.x;
     const int N = p.B * p.gamma;
-    float *sv = reinterpret_cast<float *>(dyn_lds);  // w is no longer needed
-    __syncthreads();
+    __syncthreads();  // sv may alias LDS the workgroup used before
     // combined cut: a position below its request's cutoff ranks below every
     // eligible one, and the budget is capped by the eligible count
     const bool combined = p.mode == DSPARK_CUT_COMBINED;
@@ -202,6 +222,51 @@ __global__ __launch_bounds__(kFrontThreads) void step_front_kernel(FrontParams p
     budget_lengths(sv, nullptr, p.B, p.gamma, cut, p.lengths, scan_lds);
 }
 
+template <bool kVecH, bool kLdsW, bool kVecV, int kRootUnroll>
+__global__ __launch_bounds__(kFrontThreads) void step_front_kernel(FrontParams p) {
+    extern __shared__ __align__(16) uint16_t dyn_lds[];
+    __shared__ float z_s[DSPARK_MAX_GAMMA], p_s[DSPARK_MAX_GAMMA], s_s[DSPARK_MAX_GAMMA];
+    __shared__ uint32_t hist[4 * 256], sh[4];
+    __shared__ int scan_lds[17];
+    __shared__ int last_s;
+    if ((int)blockIdx.x >= p.B) {
+        const int nw = blockDim.x / kWave;
+        front_root_rows<kVecV, kRootUnroll, false>(
+            p, (int64_t)((int)blockIdx.x - p.B) * nw + threadIdx.x / kWave,
+            (int64_t)((int)gridDim.x - p.B) * nw);
+        return;
+    }
+    const int b = blockIdx.x;
+    const int tid = threadIdx.x;
+    if (tid == 0)
+        __hip_atomic_store(p.req_arrivals + b, (uint64_t)0, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+    const uint16_t *wp = p.w;
+    if (kLdsW) {
+        stage_w(p.w, p.d, dyn_lds);
+        __syncthreads();
+        wp = dyn_lds;
+    }
+    // the select reads survival from another workgroup of this grid
+    const bool select_here = p.arrivals != nullptr;
+    front_request<kVecH>(p, wp, b, select_here, false, z_s, p_s, s_s);
+    if (!select_here) return;
+
+    // budget: count this request as done once its survival stores are complete;
+    // the workgroup that counts the last request picks for the whole batch
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    if (tid == 0) {
+        const unsigned old = __hip_atomic_fetch_add(p.arrivals, 1u, __ATOMIC_RELAXED,
+                                                    __HIP_MEMORY_SCOPE_AGENT);
+        last_s = old == (unsigned)(p.B - 1);
+    }
+    __syncthreads();
+    if (!last_s) return;
+    if (tid == 0) __hip_atomic_store(p.arrivals, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    front_pick(p, reinterpret_cast<float *>(dyn_lds), hist, sh, scan_lds);  // w is no longer needed
+}
+
 // ----------------------------------------------------------------- stream
 
 struct StreamParams {
@@ -211,10 +276,10 @@ struct StreamParams {
     int B, gamma, V;
     int32_t *cu, *ptok, *psrc, *pam, *acc, *bonus;
     uint64_t *keys;
-    const uint64_t *rkeys;  // root-row keys from the front kernel
-    uint64_t *arrivals;     // [B] draft slots streamed per request, zeroed by the front
+    const uint64_t *rkeys;  // root-row keys
+    uint64_t *arrivals;     // [B] streamed slots per request (zero between calls)
     int target_waves;       // sub-chunk length: about one sub-chunk per target wave
-    int root_waves;         // waves that streamed the root rows in the front kernel
+    int root_waves;         // waves that streamed the root rows
 };
 
 // Largest b in [0, B] with cu[b] - b <= r, i.e. the request that owns draft
@@ -229,19 +294,17 @@ __device__ __forceinline__ int draft_owner(const int *cu, int B, int64_t r) {
     return lo;
 }
 
-template <bool kVec>
-__global__ __launch_bounds__(kStreamThreads) void step_stream_kernel(StreamParams p) {
-    extern __shared__ int smem[];
-    int *len_s = smem;          // [B]
-    int *cu_s = smem + p.B;     // [B + 1]
-    __shared__ int scan_lds[17];
-    const int B = p.B, g = p.gamma, g1 = p.gamma + 1;
-    const int tid = threadIdx.x, bd = blockDim.x;
-    const int lane = tid & (kWave - 1);
-
-    // schedule: lengths (clamped), cu_seqlens in LDS, this workgroup's outputs
+// Verify lengths (clamped to [0, gamma]) and cu_seqlens into LDS. Every thread
+// calls it. kCoherent: the lengths were written by other workgroups of this
+// same grid.
+template <bool kCoherent>
+__device__ __forceinline__ void lengths_to_lds(const StreamParams &p, int *len_s, int *cu_s,
+                                               int *scan_lds) {
+    const int B = p.B, g = p.gamma, tid = threadIdx.x, bd = blockDim.x;
     for (int b = tid; b < B; b += bd) {
-        const int L = p.lengths[b];
+        const int L = kCoherent ? __hip_atomic_load(const_cast<int32_t *>(p.lengths + b),
+                                                    __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                                : p.lengths[b];
         len_s[b] = L < 0 ? 0 : (L > g ? g : L);
     }
     __syncthreads();
@@ -256,7 +319,14 @@ __global__ __launch_bounds__(kStreamThreads) void step_stream_kernel(StreamParam
     }
     if (tid == 0) cu_s[B] = carry;
     __syncthreads();
-    for (int b = blockIdx.x; b < B; b += gridDim.x) {
+}
+
+// The schedule outputs (cu_seqlens, packed tokens and source rows) of
+// requests wg, wg + nwg, ...
+__device__ __forceinline__ void write_schedule(const StreamParams &p, const int *len_s,
+                                               const int *cu_s, int wg, int nwg) {
+    const int g1 = p.gamma + 1, tid = threadIdx.x, bd = blockDim.x;
+    for (int b = wg; b < p.B; b += nwg) {
         if (tid == 0) {
             p.cu[b + 1] = cu_s[b + 1];
             if (b == 0) p.cu[0] = 0;
@@ -266,75 +336,290 @@ __global__ __launch_bounds__(kStreamThreads) void step_stream_kernel(StreamParam
             p.psrc[cu_s[b] + j] = b * g1 + j;
         }
     }
+}
 
-    // draft rows in sub-chunks of about equal length, one per target wave,
-    // dealt out cyclically: wave w of W streams sub-chunks w, w + W, ...
-    // Long contiguous runs per wave keep the HBM row buffers better used than
-    // many short interleaved ones.
+// Counts n more streamed slots of a request on its arrival counter once the
+// calling wave's key stores are complete. True on the wave whose count
+// reaches `target` (the request's last contribution); that wave also returns
+// the counter to zero for the next call. Called by a whole wave; no waiting.
+__device__ __forceinline__ bool arrive_last(uint64_t *cnt, int64_t n, int64_t target) {
+    const int lane = threadIdx.x & (kWave - 1);
+    __builtin_amdgcn_s_waitcnt(0);  // the key stores are at the coherence point
+    unsigned long long old = 0;
+    if (lane == 0)
+        old = __hip_atomic_fetch_add(cnt, (uint64_t)n, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    old = __shfl(old, 0, kWave);
+    const bool last = (int64_t)old + n == target;
+    if (last && lane == 0)
+        __hip_atomic_store(cnt, (uint64_t)0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return last;
+}
+
+// Acceptance and bonus of request b by the calling wave: the root row's
+// argmax from the root keys (kRootCoherent: written by this same grid), the
+// draft rows' from the draft keys of sub-chunk length K.
+template <bool kRootCoherent>
+__device__ __forceinline__ void accept_request(const StreamParams &p, const int *len_s,
+                                               const int *cu_s, int b, int64_t Vv, int64_t K,
+                                               int64_t Kr) {
+    const int start = cu_s[b];
+    const int dstart = start - b;  // first draft row of request b
+    wave_accept_rows(
+        [&](int j) {
+            return j == 0 ? row_argmax<kRootCoherent>(p.rkeys, b, Vv, Kr)
+                          : row_argmax<true>(p.keys, dstart + j - 1, Vv, K);
+        },
+        len_s[b] + 1, p.gamma, p.tokens + (size_t)b * (p.gamma + 1), p.pam + start, p.acc + b,
+        p.bonus + b);
+}
+
+// Slots [e, e_end) of the draft rows of all requests laid end to end (Vv
+// slots per row), streamed by the calling wave as sub-chunk s: each row
+// segment leaves one key at keys[s + r]; arrive(b, n) counts the n slots of
+// request b streamed, once at each change of request and at the end.
+template <bool kVec, int kUnroll, typename Arrive>
+__device__ __forceinline__ void stream_draft_span(const StreamParams &p, const int *cu_s,
+                                                  int64_t Vv, int64_t s, int64_t e, int64_t e_end,
+                                                  Arrive arrive) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const int g1 = p.gamma + 1;
+    int64_t r = e / Vv;
+    int cur_b = -1;    // request of the rows being streamed
+    int64_t done = 0;  // its slots streamed in this sub-chunk
+    while (e < e_end) {
+        const int64_t row_end = (r + 1) * Vv;
+        const int64_t seg_end = e_end < row_end ? e_end : row_end;
+        const int b = draft_owner(cu_s, p.B, r);
+        if (b != cur_b) {
+            if (cur_b >= 0) arrive(cur_b, done);
+            cur_b = b;
+            done = 0;
+        }
+        const int64_t src = (int64_t)b * g1 + 1 + (r - (cu_s[b] - b));
+        float best = -INFINITY;
+        int bidx = -1;
+        lane_row_segment<kVec, kUnroll>(p.logits + (size_t)src * (size_t)p.V, e - r * Vv,
+                                        seg_end - r * Vv, lane, best, bidx);
+        uint64_t key = bidx >= 0 ? argmax_key(best, (uint32_t)bidx) : 0ull;
+        key = wave_max_u64(key);
+        if (lane == 0) store_key_coherent(p.keys + s + r, key);
+        done += seg_end - e;
+        e = seg_end;
+        ++r;
+    }
+    if (cur_b >= 0) arrive(cur_b, done);
+}
+
+// The draft rows (E slots) in sub-chunks of K slots dealt cyclically: wave w
+// of W streams sub-chunks w, w + W, ... Long contiguous runs per wave keep the
+// HBM row buffers better used than many short interleaved ones.
+template <bool kVec, typename Arrive>
+__device__ __forceinline__ void stream_draft_rows(const StreamParams &p, const int *cu_s,
+                                                  int64_t Vv, int64_t E, int64_t K, int64_t w,
+                                                  int64_t W, Arrive arrive) {
+    const int64_t NS = (E + K - 1) / K;
+    for (int64_t cur = w; cur < NS; cur += W)
+        stream_draft_span<kVec, kStreamUnroll>(p, cu_s, Vv, cur, cur * K,
+                                               cur * K + K < E ? cur * K + K : E, arrive);
+}
+
+template <bool kVec>
+__global__ __launch_bounds__(kStreamThreads) void step_stream_kernel(StreamParams p) {
+    extern __shared__ int smem[];
+    int *len_s = smem;          // [B]
+    int *cu_s = smem + p.B;     // [B + 1]
+    __shared__ int scan_lds[17];
+    const int B = p.B, tid = threadIdx.x, nw = blockDim.x / kWave;
+
+    // schedule: lengths (clamped), cu_seqlens in LDS, this workgroup's outputs
+    lengths_to_lds<false>(p, len_s, cu_s, scan_lds);
+    write_schedule(p, len_s, cu_s, blockIdx.x, gridDim.x);
+
     const int64_t Vv = kVec ? (p.V >> 3) : p.V;
     const int64_t E = (int64_t)(cu_s[B] - B) * Vv;
     const int64_t K = sub_len(E, p.target_waves);
     const int64_t Kr = sub_len((int64_t)B * Vv, p.root_waves);
-    const int64_t NS = (E + K - 1) / K;
-    const int64_t W = (int64_t)gridDim.x * (bd / kWave);
+    // requests without draft rows are finished by the workgroup that owns them
+    if (tid < kWave)
+        for (int b = blockIdx.x; b < B; b += gridDim.x)
+            if (len_s[b] == 0) accept_request<false>(p, len_s, cu_s, b, Vv, K, Kr);
+    // the wave that completes a request's draft rows finishes it
+    stream_draft_rows<kVec>(p, cu_s, Vv, E, K, (int64_t)blockIdx.x * nw + tid / kWave,
+                            (int64_t)gridDim.x * nw, [&](int b, int64_t n) {
+                                if (arrive_last(p.arrivals + b, n, (int64_t)len_s[b] * Vv))
+                                    accept_request<false>(p, len_s, cu_s, b, Vv, K, Kr);
+                            });
+}
 
-    // acceptance and bonus of request b by the calling wave: the root row's
-    // argmax from the front kernel's keys, the draft rows' from this kernel's
-    auto accept = [&](int b) {
+// ---------------------------------------------------------------- one launch
+
+// The whole step in one grid (threshold and static cuts, whose lengths need
+// no batch-wide pick) of three kinds of workgroup, in this order: request
+// workgroups (the GEMV, survival and length of requests g, g + gemv_wgs, ...),
+// root workgroups (the root rows, while the GEMV runs) and, when the draft
+// stream wants more waves, plain stream workgroups. Once every length is
+// final, all of them stream the draft rows. The only wait is for the lengths,
+// which only request workgroups write; they come first in the grid and never
+// wait before their lengths are out, and the grid is sized to be resident at
+// once, so they all run. The wait is bounded; a workgroup that gives up sets a
+// flag and leaves.
+struct OneParams {
+    FrontParams f;
+    StreamParams s;
+    unsigned *gemv_done;  // request workgroups done (zero between calls)
+    unsigned *go;         // set to the grid size once every length is final; each
+                          // workgroup takes one off as it exits (zero between calls)
+    unsigned *timed_out;  // set when a workgroup gave up waiting for the lengths
+    int gemv_wgs, root_wgs;
+    int64_t lead;         // draft slots more per early wave than per root wave
+};
+
+// The draft rows of the one-launch step, laid end to end (E slots), as one
+// sub-chunk per wave in two regions: the first NA sub-chunks, of KA slots, go
+// to the early waves (request and plain stream workgroups, free once the
+// lengths are final), the others, of KB = KA - lead slots, to the root-row
+// waves, which reach the drafts later. Sub-chunk s keeps the key of its
+// segment inside row r at keys[s + r]: s + r still rises by one at every
+// sub-chunk or row boundary, so no two segments share a key.
+struct SplitLayout {
+    int64_t KA, KB, EA, NA, E;
+    __device__ __forceinline__ SplitLayout(int64_t E_, int64_t WA, int64_t W, int64_t lead) {
+        E = E_;
+        const int64_t kb = (E - WA * lead + W - 1) / W;
+        KB = kb < kSubMin ? kSubMin : kb;
+        KA = KB + lead;
+        EA = WA * KA < E ? WA * KA : E;
+        NA = (EA + KA - 1) / KA;
+    }
+    __device__ __forceinline__ int64_t sub(int64_t e) const {
+        return e < EA ? e / KA : NA + (e - EA) / KB;
+    }
+    // slots of sub-chunk s: [*e0, *e1), empty past the end
+    __device__ __forceinline__ void span(int64_t s, int64_t *e0, int64_t *e1) const {
+        int64_t a, b;
+        if (s < NA) {
+            a = s * KA;
+            b = a + KA < EA ? a + KA : EA;
+        } else {
+            a = EA + (s - NA) * KB;
+            b = a + KB < E ? a + KB : E;
+        }
+        *e0 = a < E ? a : E;
+        *e1 = b;
+    }
+};
+
+// Upper bound of the wait for the lengths in ticks of the 100 MHz constant
+// clock (1 s; the lengths normally follow the slowest GEMV by microseconds).
+constexpr unsigned long long kWaitTicks = 100000000ull;
+
+template <bool kVecH, bool kLdsW, bool kVecV>
+__global__ __launch_bounds__(kFrontThreads) void step_one_kernel(OneParams q) {
+    extern __shared__ __align__(16) uint16_t dyn_lds[];
+    __shared__ float z_s[DSPARK_MAX_GAMMA], p_s[DSPARK_MAX_GAMMA], s_s[DSPARK_MAX_GAMMA];
+    __shared__ int scan_lds[17];
+    __shared__ int last_s, ok_s;
+    const FrontParams &p = q.f;
+    const StreamParams &sp = q.s;
+    const int tid = threadIdx.x, nw = blockDim.x / kWave, wave = tid / kWave;
+    const int wg = blockIdx.x, G = gridDim.x, B = p.B;
+    const int64_t Vv = kVecV ? (p.V >> 3) : p.V;
+    const int64_t root_waves = (int64_t)q.root_wgs * nw;
+    const bool is_root = wg >= q.gemv_wgs && wg < q.gemv_wgs + q.root_wgs;
+    bool wait = true;
+    if (wg < q.gemv_wgs) {
+        const uint16_t *wp = p.w;
+        if (kLdsW) {
+            stage_w(p.w, p.d, dyn_lds);
+            __syncthreads();
+            wp = dyn_lds;
+        }
+        for (int b = wg; b < B; b += q.gemv_wgs) {
+            front_request<kVecH, kOneGemvUnroll>(p, wp, b, false, true, z_s, p_s, s_s);
+            __syncthreads();
+        }
+        // this workgroup's length stores are at the coherence point: count it;
+        // the last to count lets every workgroup go on
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        if (tid == 0) {
+            const int last = __hip_atomic_fetch_add(q.gemv_done, 1u, __ATOMIC_RELAXED,
+                                                    __HIP_MEMORY_SCOPE_AGENT) ==
+                             (unsigned)(q.gemv_wgs - 1);
+            if (last) {
+                __hip_atomic_store(q.gemv_done, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                __hip_atomic_store(q.go, (unsigned)G, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
+            last_s = last;
+        }
+        __syncthreads();
+        wait = !last_s;
+    } else if (is_root) {
+        front_root_rows<kVecV, kOneRootUnroll, true>(p, (int64_t)(wg - q.gemv_wgs) * nw + wave,
+                                                     root_waves);
+    }
+    if (wait) {
+        if (tid == 0) {
+            const unsigned long long t0 = wall_clock64();
+            int ok = 1;
+            while (__hip_atomic_load(q.go, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0u) {
+                if (wall_clock64() - t0 > kWaitTicks) {
+                    ok = 0;
+                    break;
+                }
+                __builtin_amdgcn_s_sleep(2);
+            }
+            if (!ok)
+                __hip_atomic_store(q.timed_out, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            ok_s = ok;
+        }
+        __syncthreads();
+        if (!ok_s) return;
+    }
+
+    // every length is final: the schedule in LDS (the head staged there is no
+    // longer needed) and this workgroup's outputs
+    int *len_s = reinterpret_cast<int *>(dyn_lds);
+    int *cu_s = len_s + B;
+    lengths_to_lds<true>(sp, len_s, cu_s, scan_lds);
+    write_schedule(sp, len_s, cu_s, wg, G);
+    // draft waves: the early ones (request and plain stream workgroups) first
+    const int64_t WA = (int64_t)(G - q.root_wgs) * nw;
+    const int64_t dw = is_root ? WA + (int64_t)(wg - q.gemv_wgs) * nw + wave
+                               : (int64_t)(wg < q.gemv_wgs ? wg : wg - q.root_wgs) * nw + wave;
+    const SplitLayout lay((int64_t)(cu_s[B] - B) * Vv, WA, (int64_t)G * nw, q.lead);
+    const int64_t Kr = sub_len((int64_t)B * Vv, root_waves);
+    // a request counts its root row and its draft rows; the wave that brings
+    // the last of them finishes it: the root row's argmax from the root keys,
+    // the draft rows' from the draft keys
+    auto arrive = [&](int b, int64_t n) {
+        if (!arrive_last(sp.arrivals + b, n, (int64_t)(len_s[b] + 1) * Vv)) return;
         const int start = cu_s[b];
         const int dstart = start - b;  // first draft row of request b
         wave_accept_rows(
             [&](int j) {
-                return j == 0 ? row_argmax(p.rkeys, b, Vv, Kr)
-                              : row_argmax<true>(p.keys, dstart + j - 1, Vv, K);
+                if (j == 0) return row_argmax<true>(sp.rkeys, b, Vv, Kr);
+                const int64_t r = dstart + j - 1;
+                return segment_keys_argmax<true>(sp.keys, r, lay.sub(r * Vv),
+                                                 lay.sub((r + 1) * Vv - 1));
             },
-            len_s[b] + 1, g, p.tokens + (size_t)b * g1, p.pam + start, p.acc + b, p.bonus + b);
+            len_s[b] + 1, sp.gamma, sp.tokens + (size_t)b * (sp.gamma + 1), sp.pam + start,
+            sp.acc + b, sp.bonus + b);
     };
-    // requests without draft rows are finished by the workgroup that owns them
-    if (tid < kWave)
-        for (int b = blockIdx.x; b < B; b += gridDim.x)
-            if (len_s[b] == 0) accept(b);
-    // `n` more draft slots of request b are done and their keys stored: count
-    // them; the wave that completes the request finishes it (no waiting)
-    auto arrive = [&](int b, int64_t n) {
-        __builtin_amdgcn_s_waitcnt(0);  // the key stores are at the coherence point
-        unsigned long long old = 0;
-        if (lane == 0)
-            old = __hip_atomic_fetch_add(p.arrivals + b, (uint64_t)n, __ATOMIC_RELAXED,
-                                         __HIP_MEMORY_SCOPE_AGENT);
-        old = __shfl(old, 0, kWave);
-        if ((int64_t)old + n == (int64_t)len_s[b] * Vv) accept(b);
-    };
-    for (int64_t cur = (int64_t)blockIdx.x * (bd / kWave) + tid / kWave; cur < NS; cur += W) {
-        // stream sub-chunk `cur`: slots [cur*K, min((cur+1)*K, E)), row by row
-        int64_t e = cur * K;
-        const int64_t e_end = e + K < E ? e + K : E;
-        int64_t r = e / Vv;
-        int cur_b = -1;    // request of the rows being streamed
-        int64_t done = 0;  // its slots streamed in this sub-chunk
-        while (e < e_end) {
-            const int64_t row_end = (r + 1) * Vv;
-            const int64_t seg_end = e_end < row_end ? e_end : row_end;
-            const int b = draft_owner(cu_s, B, r);
-            if (b != cur_b) {
-                if (cur_b >= 0) arrive(cur_b, done);
-                cur_b = b;
-                done = 0;
-            }
-            const int64_t src = (int64_t)b * g1 + 1 + (r - (cu_s[b] - b));
-            float best = -INFINITY;
-            int bidx = -1;
-            lane_row_segment<kVec, kStreamUnroll>(p.logits + (size_t)src * (size_t)p.V,
-                                                  e - r * Vv, seg_end - r * Vv, lane, best, bidx);
-            uint64_t key = bidx >= 0 ? argmax_key(best, (uint32_t)bidx) : 0ull;
-            key = wave_max_u64(key);
-            if (lane == 0) store_key_coherent(p.keys + cur + r, key);
-            done += seg_end - e;
-            e = seg_end;
-            ++r;
-        }
-        if (cur_b >= 0) arrive(cur_b, done);
+    if (is_root)
+        root_segments((int64_t)B * Vv, Kr, Vv, (int64_t)(wg - q.gemv_wgs) * nw + wave, root_waves,
+                      arrive);
+    // this wave's sub-chunk: early wave dw < WA takes region A's sub-chunk dw,
+    // root wave dw takes region B's sub-chunk dw - WA
+    const int64_t s_mine = dw < WA ? (dw < lay.NA ? dw : -1) : lay.NA + (dw - WA);
+    if (s_mine >= 0) {
+        int64_t e0, e1;
+        lay.span(s_mine, &e0, &e1);
+        if (e0 < e1)
+            stream_draft_span<kVecV, kOneStreamUnroll>(sp, cu_s, Vv, s_mine, e0, e1, arrive);
     }
+    // every wave of this workgroup is past the wait
+    if (tid == 0) __hip_atomic_fetch_sub(q.go, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // ----------------------------------------------------------------- launch
@@ -384,6 +669,61 @@ static void launch_front(bool hvec, bool ldsw, const FrontParams &fp, int root_w
         launch_front_u<kVecV, kRootUnrollShallow>(hvec, ldsw, fp, root_wgs, lds, s);
     else
         launch_front_u<kVecV, kRootUnrollDeep>(hvec, ldsw, fp, root_wgs, lds, s);
+}
+
+template <bool kVecH, bool kLdsW, bool kVecV>
+static int one_capacity(size_t lds) {
+    // workgroups of the one-launch kernel resident at once for this LDS size,
+    // cached per device and 4 KiB LDS bucket
+    static std::atomic<int> cache[64][16];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+    const int bucket = (int)((lds + 4095) / 4096);
+    if (bucket >= 16) return 0;
+    int cap = cache[dev][bucket].load(std::memory_order_relaxed);
+    if (cap > 0) return cap;
+    int blocks = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, step_one_kernel<kVecH, kLdsW, kVecV>,
+                                                     kFrontThreads, (size_t)bucket * 4096) !=
+            hipSuccess ||
+        blocks < 0)
+        blocks = 0;
+    cap = blocks * device_cu_count();
+    if (cap > 0) cache[dev][bucket].store(cap, std::memory_order_relaxed);
+    return cap;
+}
+
+// Launches the one-launch step when its whole grid fits on the device at once;
+// *done tells whether it did.
+template <bool kVecH, bool kLdsW, bool kVecV>
+static hipError_t launch_one_v(const OneParams &q, int grid, size_t lds, hipStream_t s,
+                               hipEvent_t ev_start, hipEvent_t ev_stop, bool *done) {
+    *done = false;
+    if (grid > one_capacity<kVecH, kLdsW, kVecV>(lds)) return hipSuccess;
+    hipError_t e;
+    if (ev_start && (e = hipEventRecord(ev_start, s)) != hipSuccess) return e;
+    hipLaunchKernelGGL((step_one_kernel<kVecH, kLdsW, kVecV>), dim3(grid), dim3(kFrontThreads),
+                       lds, s, q);
+    e = hipGetLastError();
+    if (e == hipSuccess && ev_stop) e = hipEventRecord(ev_stop, s);
+    *done = e == hipSuccess;
+    return e;
+}
+
+template <bool kVecV>
+static hipError_t launch_one(bool hvec, bool ldsw, const OneParams &q, int grid, size_t lds,
+                             hipStream_t s, hipEvent_t ev_start, hipEvent_t ev_stop, bool *done) {
+    if (hvec && ldsw)
+        return launch_one_v<true, true, kVecV>(q, grid, lds, s, ev_start, ev_stop, done);
+    if (hvec) return launch_one_v<true, false, kVecV>(q, grid, lds, s, ev_start, ev_stop, done);
+    return launch_one_v<false, false, kVecV>(q, grid, lds, s, ev_start, ev_stop, done);
+}
+
+// Whether the caller asked for the two-launch form (DSPARK_STEP_LAUNCHES=2 in
+// the environment), e.g. to compare or test both.
+static bool two_launches_forced() {
+    const char *v = getenv("DSPARK_STEP_LAUNCHES");
+    return v != nullptr && v[0] == '2' && v[1] == '\0';
 }
 
 hipError_t launch_fused_step(const uint16_t *hidden, const uint16_t *w, float bias,
@@ -438,19 +778,7 @@ hipError_t launch_fused_step(const uint16_t *hidden, const uint16_t *w, float bi
     if (root_wgs * (kFrontThreads / kWave) > kMaxWaves) root_wgs = kMaxWaves / (kFrontThreads / kWave);
     root_wgs = root_wgs < 1 ? 1 : root_wgs;
     const int root_waves = (int)root_wgs * (kFrontThreads / kWave);
-    if (vvec)
-        launch_front<true>(hvec, ldsw, fp, (int)root_wgs, front_lds, s);
-    else
-        launch_front<false>(hvec, ldsw, fp, (int)root_wgs, front_lds, s);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
 
-    if ((mode == DSPARK_CUT_BUDGET || mode == DSPARK_CUT_COMBINED) && !select_in_front) {
-        e = launch_schedule(surv, B, gamma, mode, cutoff, budget, lengths, s);
-        if (e != hipSuccess) return e;
-    }
-
-    const size_t lds = (size_t)(2 * B + 1) * sizeof(int);
     StreamParams p;
     p.logits = logits;
     p.tokens = tokens;
@@ -469,13 +797,54 @@ hipError_t launch_fused_step(const uint16_t *hidden, const uint16_t *w, float bi
     p.arrivals = rcnt;
     p.target_waves = kStreamWavesPerCU * cus < kMaxWaves ? kStreamWavesPerCU * cus : (int)kMaxWaves;
     p.root_waves = root_waves;
-    // stream grid: enough workgroups for the target waves, at most the resident
-    // ones, and no more than the largest possible draft rows (every request at
-    // gamma) fill with minimum-length sub-chunks
+    // stream workgroups: enough for the target waves, and no more than the
+    // largest possible draft rows (every request at gamma) fill with
+    // minimum-length sub-chunks
     int stream_wgs_needed = (p.target_waves + kStreamThreads / kWave - 1) / (kStreamThreads / kWave);
     const int64_t max_sub = ((int64_t)B * gamma * Vv + kSubMin - 1) / kSubMin;
     const int64_t max_wgs = (max_sub + kStreamThreads / kWave - 1) / (kStreamThreads / kWave);
     if (max_wgs < stream_wgs_needed) stream_wgs_needed = max_wgs < 1 ? 1 : (int)max_wgs;
+
+    // one launch (threshold and static cuts): request workgroups (one per CU
+    // at most, each looping over its requests), the root workgroups, and plain
+    // stream workgroups up to the stream's target, when the whole grid is
+    // resident at once and its waves fit the key layout
+    if ((mode == DSPARK_CUT_THRESHOLD || mode == DSPARK_CUT_STATIC) && !two_launches_forced()) {
+        OneParams q;
+        q.f = fp;
+        q.s = p;
+        q.gemv_done = arrivals;
+        q.go = reinterpret_cast<unsigned *>(wsb + ws_ctrl_offset() + kCtrlGoOffset);
+        q.timed_out = reinterpret_cast<unsigned *>(wsb + ws_ctrl_offset() + kCtrlTimedOutOffset);
+        q.gemv_wgs = B < cus ? B : cus;
+        q.root_wgs = (int)root_wgs;
+        q.lead = (int64_t)(kLead * (double)((int64_t)B * Vv / root_waves));
+        int grid = q.gemv_wgs + q.root_wgs;
+        if (grid < stream_wgs_needed) grid = stream_wgs_needed;
+        size_t lds = ldsw ? (size_t)d * 2 : 0;
+        if ((size_t)(2 * B + 1) * 4 > lds) lds = (size_t)(2 * B + 1) * 4;
+        if ((int64_t)grid * (kFrontThreads / kWave) <= kMaxWaves) {
+            bool done = false;
+            const hipError_t e =
+                vvec ? launch_one<true>(hvec, ldsw, q, grid, lds, s, ev_start, ev_stop, &done)
+                     : launch_one<false>(hvec, ldsw, q, grid, lds, s, ev_start, ev_stop, &done);
+            if (e != hipSuccess || done) return e;
+        }
+    }
+
+    if (vvec)
+        launch_front<true>(hvec, ldsw, fp, (int)root_wgs, front_lds, s);
+    else
+        launch_front<false>(hvec, ldsw, fp, (int)root_wgs, front_lds, s);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+
+    if ((mode == DSPARK_CUT_BUDGET || mode == DSPARK_CUT_COMBINED) && !select_in_front) {
+        e = launch_schedule(surv, B, gamma, mode, cutoff, budget, lengths, s);
+        if (e != hipSuccess) return e;
+    }
+
+    const size_t lds = (size_t)(2 * B + 1) * sizeof(int);
     int g = vvec ? stream_grid<true>(lds) : stream_grid<false>(lds);
     g = g < stream_wgs_needed ? g : stream_wgs_needed;
     // measurement events bracket the dominant kernel (the draft-row stream)

@@ -259,11 +259,22 @@ dspark_status dspark_cap_accept(const int32_t *packed_argmax_full, const int32_t
  * packed_argmax and accepted feed dspark_cap_accept for the audit arm).
  * conf and survival may be NULL when the caller does not want them. ws must be
  * zero-filled before its first use with this entry point (dspark_workspace_init
- * does it on a stream): its first 256 bytes hold a control word that every
- * call returns to zero on completion, at the same offset for every size, so
- * one workspace serves calls of any sizes it is large enough for. The rest is
- * scratch. Calls that share a workspace must not overlap in time. Batches
- * above 4096 requests run the same step through the stage kernels.
+ * does it on a stream): its first 256 bytes hold control words and the next
+ * 32 KiB per-request counters, which every call returns to zero on completion,
+ * at the same offsets for every size, so one workspace serves calls of any
+ * sizes it is large enough for. The rest is scratch. Calls that share a
+ * workspace must not overlap in time. Batches above 4096 requests run the same
+ * step through the stage kernels.
+ *
+ * Threshold and static cuts run in one launch whose workgroups wait once, for
+ * the verify lengths that its first workgroups compute; the grid is sized to
+ * be resident on the device at once (otherwise the step takes two launches).
+ * That wait is bounded (about one second): a workgroup that gives up sets the
+ * 32-bit word at byte 192 of ws to 1 and leaves; the outputs of that call are
+ * then undefined and ws must be initialised again. It does not happen while
+ * the device runs nothing else that holds its compute units for that long.
+ * DSPARK_STEP_LAUNCHES=2 in the environment selects the two-launch form for
+ * every cut (same results).
  */
 dspark_status dspark_step(const dspark_bf16 *hidden, const dspark_bf16 *w, float bias,
                           const float *temps, const int32_t *tokens, const dspark_bf16 *logits,
@@ -275,10 +286,10 @@ dspark_status dspark_step(const dspark_bf16 *hidden, const dspark_bf16 *w, float
 
 /*
  * Measurement aid: dspark_step, plus hipEventRecord(ev_start, stream) right
- * before the launch of the step's dominant kernel (the stream over the draft
- * rows, which also writes the acceptance) and hipEventRecord(ev_stop, stream)
- * right after it, so the elapsed time between the two events is that kernel's
- * duration. ev_start / ev_stop are hipEvent_t handles (as void*) the caller
+ * before the launch of the step's dominant kernel (in one launch, the whole
+ * step; in two, the stream over the draft rows, which also writes the
+ * acceptance) and hipEventRecord(ev_stop, stream) right after it, so the
+ * elapsed time between the two events is that kernel's duration. ev_start / ev_stop are hipEvent_t handles (as void*) the caller
  * created with timing enabled; either may be NULL. Results are identical to
  * dspark_step's; nothing is allocated.
  */

@@ -1,0 +1,94 @@
+"""The fused step's two forms (needs an MI355X).
+
+Threshold and static cuts normally run the whole step in one launch; the
+environment variable DSPARK_STEP_LAUNCHES=2 selects the two-launch form (the
+one budget cuts use). Both must match the oracle, match each other bit for
+bit, and leave the workspace's counters at zero, so that calls of either form
+can follow each other on one workspace.
+"""
+import numpy as np
+import pytest
+import torch
+
+import __graft_entry__  # noqa: F401
+import confidence_scheduled_ragged_amd as dspark
+from parity_utils import compare, oracle_back, oracle_front, snapshot
+from synth import CONFIGS, make_step
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda:0"
+CTRL_BYTES = 256       # control words at the start of the workspace
+MAX_FUSED_B = 4096     # per-request counters that follow them (uint64 each)
+
+
+def _host(out):
+    return {k: v.cpu().numpy() for k, v in out.items()}
+
+
+def _step(s, ws, two_launches, monkeypatch):
+    if two_launches:
+        monkeypatch.setenv("DSPARK_STEP_LAUNCHES", "2")
+    else:
+        monkeypatch.delenv("DSPARK_STEP_LAUNCHES", raising=False)
+    out = dspark.dspark_step(s.hidden, s.w, s.bias, s.temps, s.tokens, s.logits, s.cfg.mode,
+                             cutoff=s.cutoff, budget=s.budget, ws=ws)
+    torch.cuda.synchronize()
+    monkeypatch.delenv("DSPARK_STEP_LAUNCHES", raising=False)
+    return _host(out)
+
+
+def _fresh_ws(cfg):
+    n = dspark.dspark_workspace_bytes(cfg.B, cfg.gamma, cfg.V)
+    ws = torch.empty(n, dtype=torch.uint8, device=DEV)
+    ws.fill_(0xA5)          # the init call must clear it
+    dspark.dspark_workspace_init(ws)
+    return ws
+
+
+def _counters_zero(ws, B):
+    head = ws[: CTRL_BYTES + 8 * min(B, MAX_FUSED_B)].cpu().numpy()
+    return int(np.count_nonzero(head)) == 0
+
+
+CASES = {
+    "tiny": CONFIGS["tiny"],
+    "mixed_threshold": CONFIGS["mixed_threshold"].scaled(V=32768),
+    "static": CONFIGS["tiny"].scaled(mode="static"),
+    "max_gamma": CONFIGS["tiny"].scaled(gamma=256, B=2, V=512, d=64),
+    "odd_vocab": CONFIGS["tiny"].scaled(V=1001, d=250),
+    "wide_batch": CONFIGS["tiny"].scaled(B=700, gamma=4, d=64, V=256),
+}
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_both_forms_match_the_oracle_and_each_other(name, monkeypatch):
+    cfg = CASES[name]
+    ws = _fresh_ws(cfg)
+    for step in range(2):
+        s = make_step(cfg, step, device=DEV)
+        one = _step(s, ws, False, monkeypatch)
+        assert _counters_zero(ws, cfg.B), f"{name}: counters left set by the one-launch form"
+        two = _step(s, ws, True, monkeypatch)
+        assert _counters_zero(ws, cfg.B), f"{name}: counters left set by the two-launch form"
+        for k in one:
+            assert np.array_equal(one[k], two[k]), f"{name} step {step}: {k} differs between forms"
+        h = snapshot(s)
+        front = oracle_front(h)
+        rows = s.host_rows(front[5][: int(front[3][-1])])
+        compare(one, oracle_back(h, front, rows), h.tokens, ctx=f"{name} step {step}")
+
+
+def test_forms_alternate_on_one_workspace(monkeypatch):
+    # one form after the other, repeatedly, on the same workspace: each call
+    # must start from the counters the previous one returned to zero
+    cfg = CONFIGS["mixed_threshold"].scaled(B=64, V=16384)
+    ws = _fresh_ws(cfg)
+    steps = [make_step(cfg, i, device=DEV) for i in range(3)]
+    ref = [_step(s, ws, False, monkeypatch) for s in steps]
+    for rnd in range(4):
+        for i, s in enumerate(steps):
+            got = _step(s, ws, (rnd + i) % 2 == 1, monkeypatch)
+            for k in got:
+                assert np.array_equal(got[k], ref[i][k]), f"round {rnd} step {i}: {k}"
+    assert _counters_zero(ws, cfg.B)
