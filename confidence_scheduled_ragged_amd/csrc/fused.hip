@@ -61,6 +61,12 @@ constexpr int kStreamUnroll = 2;  // 16-byte loads in flight per lane (more wave
 // its budget arm (gamma*d = 65536 < V/2) 68.1 against 70.3; the budget
 // workload at d = 7168 (gamma*d = 114688 > V/2) 67.7 with two against 69.3.
 constexpr int kRootUnrollDeep = 4;
+// Smallest batch that takes the one-launch form by default. Below it the
+// in-grid wait for the lengths costs more than the second launch it saves
+// (measured at gamma = 16, d = 4096, V = 151936: two launches faster by about
+// 2 us at B = 1..32 and 1 us at B = 64, one launch faster by 2.4 us at
+// B = 128 and 3-5 us at B = 256).
+constexpr int kOneLaunchMinB = 96;
 // The one-launch step: 16-byte loads in flight per lane in the GEMV, the root
 // rows and the draft rows (its grid holds four waves per SIMD, so deeper
 // unrolling costs no occupancy), and the extra draft slots per early wave, as
@@ -706,11 +712,12 @@ static hipError_t launch_one_v(const OneParams &q, int grid, size_t lds, hipStre
     return e;
 }
 
-// Whether the caller asked for the two-launch form (DSPARK_STEP_LAUNCHES=2 in
-// the environment), e.g. to compare or test both.
-static bool two_launches_forced() {
+// The form the caller asked for with DSPARK_STEP_LAUNCHES in the environment
+// (1 or 2, e.g. to compare or test both), else 0: chosen by size.
+static int forced_launches() {
     const char *v = getenv("DSPARK_STEP_LAUNCHES");
-    return v != nullptr && v[0] == '2' && v[1] == '\0';
+    if (v == nullptr || v[0] == '\0' || v[1] != '\0') return 0;
+    return v[0] == '1' ? 1 : (v[0] == '2' ? 2 : 0);
 }
 
 hipError_t launch_fused_step(const uint16_t *hidden, const uint16_t *w, float bias,
@@ -792,11 +799,14 @@ hipError_t launch_fused_step(const uint16_t *hidden, const uint16_t *w, float bi
     const int64_t max_wgs = (max_sub + kStreamThreads / kWave - 1) / (kStreamThreads / kWave);
     if (max_wgs < stream_wgs_needed) stream_wgs_needed = max_wgs < 1 ? 1 : (int)max_wgs;
 
-    // one launch (threshold and static cuts): request workgroups (one per CU
-    // at most, each looping over its requests), the root workgroups, and plain
-    // stream workgroups up to the stream's target, when the whole grid is
-    // resident at once and its waves fit the key layout
-    if ((mode == DSPARK_CUT_THRESHOLD || mode == DSPARK_CUT_STATIC) && !two_launches_forced()) {
+    // one launch (threshold and static cuts, batches from kOneLaunchMinB):
+    // request workgroups (one per CU at most, each looping over its requests),
+    // the root workgroups, and plain stream workgroups up to the stream's
+    // target, when the whole grid is resident at once and its waves fit the
+    // key layout
+    const int forced = forced_launches();
+    if ((mode == DSPARK_CUT_THRESHOLD || mode == DSPARK_CUT_STATIC) && forced != 2 &&
+        (B >= kOneLaunchMinB || forced == 1)) {
         OneParams q;
         q.f = fp;
         q.s = p;

@@ -266,15 +266,16 @@ dspark_status dspark_cap_accept(const int32_t *packed_argmax_full, const int32_t
  * workspace must not overlap in time. Batches above 4096 requests run the same
  * step through the stage kernels.
  *
- * Threshold and static cuts run in one launch whose workgroups wait once, for
- * the verify lengths that its first workgroups compute; the grid is sized to
- * be resident on the device at once (otherwise the step takes two launches).
+ * Threshold and static cuts from 96 requests up run in one launch whose
+ * workgroups wait once, for the verify lengths that its first workgroups
+ * compute; the grid is sized to be resident on the device at once (otherwise,
+ * and for smaller batches and budget cuts, the step takes two launches).
  * That wait is bounded (about one second): a workgroup that gives up sets the
  * 32-bit word at byte 192 of ws to 1 and leaves; the outputs of that call are
  * then undefined and ws must be initialised again. It does not happen while
  * the device runs nothing else that holds its compute units for that long.
- * DSPARK_STEP_LAUNCHES=2 in the environment selects the two-launch form for
- * every cut (same results).
+ * DSPARK_STEP_LAUNCHES=1 or 2 in the environment selects the one- or
+ * two-launch form where both apply (same results).
  */
 dspark_status dspark_step(const dspark_bf16 *hidden, const dspark_bf16 *w, float bias,
                           const float *temps, const int32_t *tokens, const dspark_bf16 *logits,

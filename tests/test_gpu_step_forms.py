@@ -1,10 +1,11 @@
 """The fused step's two forms (needs an MI355X).
 
-Threshold and static cuts normally run the whole step in one launch; the
-environment variable DSPARK_STEP_LAUNCHES=2 selects the two-launch form (the
-one budget cuts use). Both must match the oracle, match each other bit for
-bit, and leave the workspace's counters at zero, so that calls of either form
-can follow each other on one workspace.
+Threshold and static cuts run the whole step in one launch from 96 requests
+up, in two below; the environment variable DSPARK_STEP_LAUNCHES (1 or 2)
+selects a form for any size (budget cuts always take two). Both forms must
+match the oracle, match each other bit for bit, and leave the workspace's
+counters at zero, so that calls of either form can follow each other on one
+workspace.
 """
 import numpy as np
 import pytest
@@ -27,10 +28,7 @@ def _host(out):
 
 
 def _step(s, ws, two_launches, monkeypatch):
-    if two_launches:
-        monkeypatch.setenv("DSPARK_STEP_LAUNCHES", "2")
-    else:
-        monkeypatch.delenv("DSPARK_STEP_LAUNCHES", raising=False)
+    monkeypatch.setenv("DSPARK_STEP_LAUNCHES", "2" if two_launches else "1")
     out = dspark.dspark_step(s.hidden, s.w, s.bias, s.temps, s.tokens, s.logits, s.cfg.mode,
                              cutoff=s.cutoff, budget=s.budget, ws=ws)
     torch.cuda.synchronize()
@@ -58,6 +56,9 @@ CASES = {
     "max_gamma": CONFIGS["tiny"].scaled(gamma=256, B=2, V=512, d=64),
     "odd_vocab": CONFIGS["tiny"].scaled(V=1001, d=250),
     "wide_batch": CONFIGS["tiny"].scaled(B=700, gamma=4, d=64, V=256),
+    # the largest batch of the fused step: each request workgroup runs 16
+    # requests, and cu_seqlens fills 32 KiB of LDS
+    "max_batch": CONFIGS["tiny"].scaled(B=4096, gamma=4, d=128, V=512),
 }
 
 
