@@ -52,13 +52,21 @@ __device__ __forceinline__ float wave_sum_f32(float x) {
     return x;
 }
 
-// Inclusive scan of one int per lane across a wave.
+// Inclusive scan of one int per lane across a wave (every lane active), by
+// DPP data movement: shifts by 1, 2, 4 and 8 lanes inside each row of 16, then
+// the last lane of row 0 added to row 1, of row 2 to row 3, and of row 1 (by
+// then the total of rows 0-1) to rows 2 and 3. A lane whose source falls
+// outside its row, or a row outside the row mask, adds 0. Six VALU steps
+// instead of six LDS permutes (about 120 cycles each); integer sums, so the
+// result is exact whatever the order.
 __device__ __forceinline__ int wave_incl_scan(int x, int lane) {
-#pragma unroll
-    for (int off = 1; off < kWave; off <<= 1) {
-        int y = __shfl_up(x, off, kWave);
-        if (lane >= off) x += y;
-    }
+    (void)lane;
+    x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xF, 0xF, false);  // row_shr:1
+    x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xF, 0xF, false);  // row_shr:2
+    x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xF, 0xF, false);  // row_shr:4
+    x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xF, 0xF, false);  // row_shr:8
+    x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xA, 0xF, false);  // row_bcast:15
+    x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xC, 0xF, false);  // row_bcast:31
     return x;
 }
 
@@ -100,6 +108,10 @@ __device__ __forceinline__ int64_t sub_len(int64_t E, int64_t Wt) {
 // acnt:  uint64 [kMaxFusedB]     per-request arrival counters of dspark_accept
 //                                (zero between calls: each request's last
 //                                arriver resets its own)
+// pslot: uint64 [kPickSlots]     per-position score slots of the one-launch
+//                                step with a batch-wide pick: (1 << 32) | the
+//                                score's bits once written, zero between calls
+//                                (the picking workgroup clears what it read)
 // keys:  uint64 [kMaxWaves + B*(gamma+1)] argmax segment keys of packed rows
 // rkeys: uint64 [kMaxWaves + B]  segment keys of the root rows (fused step)
 // surv:  float [B*gamma]         survival scratch (when the caller passes none)
@@ -107,6 +119,7 @@ __device__ __forceinline__ int64_t sub_len(int64_t E, int64_t Wt) {
 constexpr int64_t kMaxWaves = 16384;  // bound on waves (or sub-chunks) per pass
 constexpr int kMaxFusedB = 4096;      // largest batch of the fused step
 constexpr size_t kCtrlBytes = 256;
+constexpr int kPickSlots = 4096;      // positions B*gamma of the one-launch batch-wide pick
 // Words of the ctrl region: at 0 the arrival counter of the request
 // workgroups (both forms of the fused step); on the next 128-byte line the
 // one-launch step's count of workgroups yet to leave once the lengths are
@@ -117,7 +130,8 @@ constexpr size_t kCtrlTimedOutOffset = 192;
 inline size_t ws_ctrl_offset() { return 0; }
 inline size_t ws_rcnt_offset() { return kCtrlBytes; }
 inline size_t ws_acnt_offset() { return kCtrlBytes + (size_t)8 * kMaxFusedB; }
-inline size_t ws_keys_offset() { return kCtrlBytes + (size_t)16 * kMaxFusedB; }
+inline size_t ws_pslot_offset() { return kCtrlBytes + (size_t)16 * kMaxFusedB; }
+inline size_t ws_keys_offset() { return ws_pslot_offset() + (size_t)8 * kPickSlots; }
 inline size_t ws_rkeys_offset(int64_t B, int64_t gamma) {
     return ws_keys_offset() + (size_t)8 * (size_t)(kMaxWaves + B * (gamma + 1));
 }

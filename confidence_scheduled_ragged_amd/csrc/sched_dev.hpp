@@ -147,19 +147,32 @@ __device__ __forceinline__ BudgetCut budget_select(const float *__restrict__ sur
 // but each thread holds a contiguous run of up to kPer flat positions in
 // registers (N <= kPer * blockDim.x). Neighbouring positions of one request
 // have non-increasing survival, so their digits often repeat; equal digits of
-// consecutive positions are counted once per run, which keeps the LDS
-// histogram atomics off the few crowded bins. The four passes use four
-// histograms cleared up front, so a pass needs two barriers: after the
-// counts, and after the digit is chosen.
+// consecutive positions are counted once per run. Neighbouring threads still
+// share digits (most survival values of a batch share their top bits), so each
+// pass counts into kSelCopies copies of the histogram, picked by thread index,
+// padded to fall in different LDS banks: same-address atomics of one
+// instruction drop eightfold. Two histogram buffers alternate between passes;
+// a pass clears the one it does not use (last read by the previous pass's
+// scan), so a pass needs two barriers: after the counts, and after the digit
+// is chosen. Once the chosen digit's bin holds at most kSelDirect values
+// (usually after two passes: survival values spread over many binades), they
+// are gathered and one wave ranks them directly instead of two more passes.
+constexpr int kSelCopies = 8;
+constexpr int kSelBinsPad = 257;
+constexpr int kSelHistWords = 2 * kSelCopies * kSelBinsPad;
+constexpr int kSelDirect = 64;
+constexpr int kSelShWords = 8;
+
 template <int kPer>
 __device__ __forceinline__ BudgetCut budget_select_runs(const float *__restrict__ surv, int N, int t,
-                                                        uint32_t *hist /*4*256*/,
-                                                        uint32_t *sh /*2*/) {
+                                                        uint32_t *hist /*kSelHistWords*/,
+                                                        uint32_t *sh /*kSelShWords*/) {
     const int tid = threadIdx.x;
     const int bd = blockDim.x;
     const int lane = tid & (kWave - 1);
     const int per = (N + bd - 1) / bd;
     const int f0 = tid * per;
+    const int copy = (tid & (kSelCopies - 1)) * kSelBinsPad;
     uint32_t v[kPer];
     int nv = 0;
 #pragma unroll
@@ -169,13 +182,17 @@ __device__ __forceinline__ BudgetCut budget_select_runs(const float *__restrict_
         v[j] = ok ? ordered_f32(surv[f]) : 0u;
         nv += ok ? 1 : 0;
     }
-    for (int i = tid; i < 4 * 256; i += bd) hist[i] = 0;
+    for (int i = tid; i < kSelHistWords; i += bd) hist[i] = 0;
     __syncthreads();
     uint32_t prefix = 0, mask = 0;
     uint32_t remaining = (uint32_t)t;
     for (int pass = 0; pass < 4; ++pass) {
         const int shift = 24 - 8 * pass;
-        uint32_t *h = hist + 256 * pass;
+        uint32_t *h = hist + (pass & 1) * (kSelCopies * kSelBinsPad);
+        if (pass >= 1 && pass < 3) {
+            uint32_t *o = hist + ((pass + 1) & 1) * (kSelCopies * kSelBinsPad);
+            for (int i = tid; i < kSelCopies * kSelBinsPad; i += bd) o[i] = 0;
+        }
         uint32_t cur = 0xFFFFFFFFu, run = 0;
 #pragma unroll
         for (int j = 0; j < kPer; ++j) {
@@ -184,39 +201,81 @@ __device__ __forceinline__ BudgetCut budget_select_runs(const float *__restrict_
                 if (dg == cur) {
                     ++run;
                 } else {
-                    if (run) atomicAdd(&h[cur], run);
+                    if (run) atomicAdd(&h[copy + cur], run);
                     cur = dg;
                     run = 1;
                 }
             }
         }
-        if (run) atomicAdd(&h[cur], run);
+        if (run) atomicAdd(&h[copy + cur], run);
         __syncthreads();
         if (tid < kWave) {
+            // lane l owns digits 255-4l .. 252-4l (descending), summed over the copies
             uint32_t c[4];
             uint32_t tot = 0;
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-                c[q] = h[255 - 4 * lane - q];
-                tot += c[q];
+                const int dg = 255 - 4 * lane - q;
+                uint32_t n = 0;
+#pragma unroll
+                for (int k = 0; k < kSelCopies; ++k) n += h[k * kSelBinsPad + dg];
+                c[q] = n;
+                tot += n;
             }
             const int inc = wave_incl_scan((int)tot, lane);
             uint32_t cum = (uint32_t)inc - tot;
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
                 if (cum < remaining && remaining <= cum + c[q]) {
-                    sh[2 * (pass & 1)] = prefix | ((uint32_t)(255 - 4 * lane - q) << shift);
-                    sh[2 * (pass & 1) + 1] = remaining - cum;
+                    sh[4 * (pass & 1)] = prefix | ((uint32_t)(255 - 4 * lane - q) << shift);
+                    sh[4 * (pass & 1) + 1] = remaining - cum;
+                    sh[4 * (pass & 1) + 2] = c[q];
                 }
                 cum += c[q];
             }
         }
         __syncthreads();
-        // the choice of this pass sits in its own pair of words, so the next
-        // pass may overwrite the other pair before every thread has read this one
-        prefix = sh[2 * (pass & 1)];
-        remaining = sh[2 * (pass & 1) + 1];
+        // the choice of this pass sits in its own words, so the next pass may
+        // overwrite the other set before every thread has read this one
+        prefix = sh[4 * (pass & 1)];
+        remaining = sh[4 * (pass & 1) + 1];
+        const uint32_t in_bin = sh[4 * (pass & 1) + 2];
         mask |= 0xFFu << shift;
+        if (pass < 3 && in_bin <= (uint32_t)kSelDirect) {
+            // the values sharing the prefix, gathered into the other (zeroed)
+            // histogram buffer: word 0 counts, words 1.. hold them
+            uint32_t *o = hist + ((pass + 1) & 1) * (kSelCopies * kSelBinsPad);
+#pragma unroll
+            for (int j = 0; j < kPer; ++j) {
+                if (j < nv && (v[j] & mask) == prefix) {
+                    const uint32_t at = atomicAdd(&o[0], 1u);
+                    if (at < (uint32_t)kSelDirect) o[1 + at] = v[j];
+                }
+            }
+            __syncthreads();
+            if (tid < kWave) {
+                // lane l ranks candidate l: the remaining-th largest is the value
+                // with fewer than `remaining` candidates above it and at least
+                // `remaining` at or above it
+                const int n = (int)in_bin;
+                const uint32_t u = lane < n ? o[1 + lane] : 0u;
+                int gt = 0, ge = 0;
+                for (int m = 0; m < n; ++m) {
+                    const uint32_t w = o[1 + m];
+                    gt += w > u ? 1 : 0;
+                    ge += w >= u ? 1 : 0;
+                }
+                if (lane < n && (uint32_t)gt < remaining && remaining <= (uint32_t)ge) {
+                    sh[4 * ((pass + 1) & 1)] = u;
+                    sh[4 * ((pass + 1) & 1) + 1] = remaining - (uint32_t)gt;
+                }
+            }
+            __syncthreads();
+            BudgetCut r;
+            r.tau = sh[4 * ((pass + 1) & 1)];
+            r.need = (int)sh[4 * ((pass + 1) & 1) + 1];
+            return r;
+        }
     }
     BudgetCut r;
     r.tau = prefix;
@@ -236,10 +295,22 @@ __device__ __forceinline__ void budget_lengths(const float *__restrict__ surv,
         int b = base + threadIdx.x;
         int gt = 0, eq = 0;
         if (b < B) {
-            for (int k = 0; k < gamma; ++k) {
-                uint32_t u = ordered_f32(ranked_value(surv, cutoff, gamma, b * gamma + k));
-                gt += u > cut.tau ? 1 : 0;
-                eq += u == cut.tau ? 1 : 0;
+            if (!cutoff && (gamma & 3) == 0 && ((uintptr_t)surv & 15) == 0) {
+                // four values per LDS access
+                const float4 *s4 = reinterpret_cast<const float4 *>(surv + (size_t)b * gamma);
+                for (int k = 0; k < (gamma >> 2); ++k) {
+                    const float4 x = s4[k];
+                    const uint32_t u0 = ordered_f32(x.x), u1 = ordered_f32(x.y),
+                                   u2 = ordered_f32(x.z), u3 = ordered_f32(x.w);
+                    gt += (u0 > cut.tau) + (u1 > cut.tau) + (u2 > cut.tau) + (u3 > cut.tau);
+                    eq += (u0 == cut.tau) + (u1 == cut.tau) + (u2 == cut.tau) + (u3 == cut.tau);
+                }
+            } else {
+                for (int k = 0; k < gamma; ++k) {
+                    uint32_t u = ordered_f32(ranked_value(surv, cutoff, gamma, b * gamma + k));
+                    gt += u > cut.tau ? 1 : 0;
+                    eq += u == cut.tau ? 1 : 0;
+                }
             }
         }
         int tot;

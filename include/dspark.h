@@ -259,23 +259,28 @@ dspark_status dspark_cap_accept(const int32_t *packed_argmax_full, const int32_t
  * packed_argmax and accepted feed dspark_cap_accept for the audit arm).
  * conf and survival may be NULL when the caller does not want them. ws must be
  * zero-filled before its first use with this entry point (dspark_workspace_init
- * does it on a stream): its first 256 bytes hold control words and the next
- * 32 KiB per-request counters, which every call returns to zero on completion,
- * at the same offsets for every size, so one workspace serves calls of any
- * sizes it is large enough for. The rest is scratch. Calls that share a
+ * does it on a stream): its first 256 bytes hold control words, followed by
+ * 32 KiB of per-request counters of this entry point, 32 KiB of those of
+ * dspark_accept and 32 KiB of score slots, all of which every call returns to
+ * zero on completion, at the same offsets for every size, so one workspace
+ * serves calls of any sizes it is large enough for. The rest is scratch. Calls that share a
  * workspace must not overlap in time. Batches above 4096 requests run the same
  * step through the stage kernels.
  *
  * Threshold and static cuts from 96 requests up run in one launch whose
  * workgroups wait once, for the verify lengths that its first workgroups
  * compute; the grid is sized to be resident on the device at once (otherwise,
- * and for smaller batches and budget cuts, the step takes two launches).
- * That wait is bounded (about one second): a workgroup that gives up sets the
- * 32-bit word at byte 192 of ws to 1 and leaves; the outputs of that call are
- * then undefined and ws must be initialised again. It does not happen while
- * the device runs nothing else that holds its compute units for that long.
- * DSPARK_STEP_LAUNCHES=1 or 2 in the environment selects the one- or
- * two-launch form where both apply (same results).
+ * and for smaller batches and budget or combined cuts, the step takes two
+ * launches). Budget and combined cuts have a one-launch form too (B*gamma up
+ * to 4096), taken only on request: one workgroup waits for every position's
+ * score and picks while the others stream the root rows, then all wait once
+ * for the lengths. Those waits are bounded (about one second): a workgroup
+ * that gives up sets the 32-bit word at byte 192 of ws to 1 and leaves; the
+ * outputs of that call are then undefined and ws must be initialised again.
+ * It does not happen while the device runs nothing else that holds its
+ * compute units for that long. DSPARK_STEP_LAUNCHES=1 or 2 in the
+ * environment selects the one- or two-launch form where both apply (same
+ * results, bit for bit).
  */
 dspark_status dspark_step(const dspark_bf16 *hidden, const dspark_bf16 *w, float bias,
                           const float *temps, const int32_t *tokens, const dspark_bf16 *logits,
