@@ -697,14 +697,6 @@ __device__ __forceinline__ float row_logit(const uint16_t *__restrict__ h,
 // be zero on entry, behind a barrier. Nothing else is written to global
 // memory here; the score slots are cleared and the survival output written
 // after the lengths are out.
-//
-// The body runs twice, the same instructions both times. The first round
-// takes whatever scores are already there without waiting and its lengths are
-// thrown away: it runs while the last rows' scores are still on their way,
-// and it brings this code and its scalar data into the compute unit's caches.
-// Code that runs once per launch in one workgroup otherwise misses those
-// caches at every step, each miss a memory round trip behind the streaming
-// loads of the rest of the chip (measured: about 10 us for the pick when cold).
 __device__ __forceinline__ bool pick_lengths(const PickParams &q, float *sv, float *rk,
                                              int *len_s, uint32_t *hist, uint32_t *sh,
                                              int *scan_lds, int *flag_s) {
@@ -712,8 +704,7 @@ __device__ __forceinline__ bool pick_lengths(const PickParams &q, float *sv, flo
     const int tid = threadIdx.x, bd = blockDim.x;
     const int N = p.B * p.gamma, g = p.gamma;
     const unsigned long long t0 = wall_clock64();
-    for (int round = 0; round < 2; ++round) {
-        const bool wait = round == 1;
+    {
         // thread b reads request b's score slots, up to kPickChunk at a time,
         // every load issued before any is waited for; slots not yet marked are
         // read again after a short sleep. The survival product follows in
@@ -735,8 +726,7 @@ __device__ __forceinline__ bool pick_lengths(const PickParams &q, float *sv, flo
                                                    : 0ull;
 #pragma unroll
                     for (int j = 0; j < kPickChunk; ++j) {
-                        // the first round takes unmarked slots as they are
-                        if (((pending >> j) & 1u) && ((x[j] >> 32) == 1ull || !wait)) {
+                        if (((pending >> j) & 1u) && (x[j] >> 32) == 1ull) {
                             v[j] = __uint_as_float((uint32_t)x[j]);
                             pending &= ~(1u << j);
                         }
@@ -1158,9 +1148,12 @@ hipError_t launch_fused_step(const uint16_t *hidden, const uint16_t *w, float bi
     // one launch for batch-wide picks (budget and combined cuts), on request
     // only: the head by one wave per hidden row, the pick in workgroup 0 while
     // the others stream the root rows, then the draft rows. Measured slower
-    // than two launches at B = 256 (mixed workload budget arm 82 us against
-    // 69 us; d = 7168, T = 768: 79 against 68-70 us): the pick lands after the
-    // root rows, and the draft phase keeps the same tail.
+    // than two launches at B = 256 (mixed workload budget arm 76 us against
+    // 69 us; d = 7168, T = 768: 72 against 68-70 us): the pick lands after the
+    // root rows, and the draft phase keeps the same tail. The same grid as the
+    // front of two launches (head, pick and root rows only, then the stream
+    // kernel) measured no faster than the request-workgroup front either
+    // (72.8 against 69.5 us).
     if ((mode == DSPARK_CUT_BUDGET || mode == DSPARK_CUT_COMBINED) && forced == 1 &&
         N <= kPickSlots && N <= kFusedSelMax && (!hvec || d <= kFrontMaxLdsW)) {
         PickParams q;
