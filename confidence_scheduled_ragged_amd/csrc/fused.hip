@@ -642,7 +642,9 @@ __global__ __launch_bounds__(kFrontThreads) void step_one_kernel(OneParams q) {
 // finishes each request, as in step_one_kernel. Workgroup 0 waits for scores
 // that every other wave writes before it waits for anything; the others wait
 // once, for the go word that only workgroup 0 writes, and the grid is sized to
-// be resident at once, so every wait ends. Both waits are bounded.
+// be resident at once, so every wait ends. Both waits are bounded. The step
+// takes this form only on request: at B = 256 it measured slower than the
+// two launches (see the launch code).
 struct PickParams {
     FrontParams f;
     StreamParams s;
@@ -651,8 +653,8 @@ struct PickParams {
     unsigned *timed_out;  // as in OneParams
 };
 
-constexpr int kPickGemvUnroll = 16;
-constexpr int kPickChunk = 16;       // score slots of one request read together by the picker  // 16-byte hidden loads in flight per lane: d <= 8192 in one batch
+constexpr int kPickGemvUnroll = 16;  // 16-byte hidden loads in flight per lane: d <= 8192 in one batch
+constexpr int kPickChunk = 16;       // score slots of one request read together by the picker
 
 // z = w.h + bias of one hidden row by the calling wave. Each lane accumulates
 // its 16-byte slots in increasing order and the wave then sums the lanes, the
