@@ -3,8 +3,8 @@
 worked_verify_block.json is a verify step of two requests worked out by hand
 from the pages' definitions (head, survival, the three cuts, packing, greedy
 acceptance, bonus): the oracle must reproduce it (CPU), and so must the HIP
-library through the fused step in both forms and through the stage entry
-points (GPU). oracle_small_case.json holds the oracle's outputs for one
+library through the fused step in both forms (for batch-wide picks the
+one-launch form is step_pick_kernel) and through the stage entry points (GPU). oracle_small_case.json holds the oracle's outputs for one
 seeded step, written by tests/golden/make_oracle_case.py; the oracle must
 still reproduce it bit for bit, and the HIP library must match it.
 """
@@ -147,8 +147,6 @@ def test_worked_block_gpu_step(launches, monkeypatch):
     w = _load(WORKED)
     inputs = _worked_inputs(w)
     for case in w["cases"]:
-        if launches == 1 and case["mode"] == "budget":
-            continue  # budget cuts always take two launches
         g = _gpu_step(w, inputs, case, launches, monkeypatch)
         assert np.max(np.abs(g["conf"] - np.array(w["conf"]))) <= 1e-5
         assert np.max(np.abs(g["survival"] - np.array(w["survival"]))) <= 1e-5
@@ -195,8 +193,6 @@ def test_stored_case_gpu_step(launches, monkeypatch):
     s = _load(STORED)
     inputs = _stored_inputs(s)
     for case in s["cases"]:
-        if launches == 1 and case["mode"] in ("budget", "combined"):
-            continue  # batch-wide picks always take two launches
         g = _gpu_step(s, inputs, case, launches, monkeypatch)
         assert np.max(np.abs(g["conf"] - np.array(case["conf"]))) <= 1e-5
         assert np.max(np.abs(g["survival"] - np.array(case["survival"]))) <= 1e-5
