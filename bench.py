@@ -521,22 +521,47 @@ def cpu_baseline(cfg, slots, min_s=10.0, max_s=30.0):
                 seconds=el), results, host
 
 
-def check_against_oracle(results, outs):
-    """Integer outputs of the GPU's own runs of the sampled batches against the
-    oracle's results on those batches (exact); conf/survival within 1e-5."""
+def check_against_oracle(results, outs, host):
+    """Outputs of the GPU's own runs of the sampled batches against the oracle's
+    results on those batches: conf/survival within 1e-5 of fp64; the integer
+    outputs exact. A position whose fp64 survival lies within 1e-5 of its
+    request's cutoff is ambiguous (fp32 and fp64 may fall on either side):
+    such positions are counted, and lengths that differ only on requests
+    holding one make the verdict "ambiguous" (the packing, acceptance and bonus
+    of every other request must still match). Returns (verdict, count)."""
     import numpy as np
 
-    ok = True
-    for o, g in zip(results, outs):
+    verdict = True
+    n_amb = 0
+    for o, g, h in zip(results, outs, host):
         gg = {k: v.cpu().numpy() for k, v in g.items()}
-        total = int(o["cu_seqlens"][-1])
-        ok &= bool(np.max(np.abs(gg["conf"] - o["conf"])) <= 1e-5)
+        ok = bool(np.max(np.abs(gg["conf"] - o["conf"])) <= 1e-5)
         ok &= bool(np.max(np.abs(gg["survival"] - o["survival"])) <= 1e-5)
-        for k in ("lengths", "cu_seqlens", "accepted", "bonus"):
-            ok &= bool(np.array_equal(gg[k], o[k]))
-        for k in ("packed_tokens", "packed_src_row", "packed_argmax"):
-            ok &= bool(np.array_equal(gg[k][:total], o[k][:total]))
-    return ok
+        amb = np.abs(o["survival"] - h["cutoff"].astype(np.float64)[:, None]) <= 1e-5
+        n_amb += int(amb.sum())
+        flips = np.nonzero(gg["lengths"] != o["lengths"])[0]
+        if flips.size == 0:
+            total = int(o["cu_seqlens"][-1])
+            for k in ("cu_seqlens", "accepted", "bonus"):
+                ok &= bool(np.array_equal(gg[k], o[k]))
+            for k in ("packed_tokens", "packed_src_row", "packed_argmax"):
+                ok &= bool(np.array_equal(gg[k][:total], o[k][:total]))
+        else:
+            ok &= bool(np.all(amb[flips].any(axis=1)))
+            for b in range(len(gg["lengths"])):
+                if b in flips:
+                    continue
+                n = int(o["lengths"][b]) + 1
+                gs, os_ = int(gg["cu_seqlens"][b]), int(o["cu_seqlens"][b])
+                for k in ("packed_tokens", "packed_argmax"):
+                    ok &= bool(np.array_equal(gg[k][gs:gs + n], o[k][os_:os_ + n]))
+                ok &= bool(gg["accepted"][b] == o["accepted"][b])
+                ok &= bool(gg["bonus"][b] == o["bonus"][b])
+            if ok and verdict is True:
+                verdict = "ambiguous"
+        if not ok:
+            verdict = False
+    return verdict, n_amb
 
 
 def main():
@@ -646,6 +671,7 @@ def main():
     cpu = None
     cpu_all = None
     parity = None
+    n_amb = None
     if not args.no_cpu_baseline:
         log("timing the oracle on the host (bounded sample)")
         cpu, results, host = cpu_baseline(cfg_t, slots)
@@ -656,9 +682,10 @@ def main():
             dspark.dspark_step(s.hidden, s.w, s.bias, s.temps, s.tokens, s.logits, cfg_t.mode,
                                cutoff=s.cutoff, budget=s.budget, out=outs[i], ws=ws)
         torch.cuda.synchronize()
-        parity = check_against_oracle(results, outs[: len(results)])
+        parity, n_amb = check_against_oracle(results, outs[: len(results)], host)
         cpu.pop("seconds", None)
-        log(f"oracle: {cpu['value']:.1f} rows/s on 1 core; parity on sampled batches: {parity}")
+        log(f"oracle: {cpu['value']:.1f} rows/s on 1 core; parity on sampled batches: {parity} "
+            f"({n_amb} ambiguous positions)")
         if not args.no_all_cores:
             log("timing the oracle on all host cores (bounded sample)")
             cpu_all = cpu_baseline_all_cores(cfg_t, host)
@@ -730,6 +757,7 @@ def main():
         "cpu_baseline_all_cores": cpu_all,
         "stream_read_context": context,
         "parity_on_sampled_batches": parity,
+        "ambiguous_positions_sampled": n_amb,
         "arms": extra,
     }
     print(json.dumps(line), flush=True)
