@@ -1,14 +1,18 @@
 """The oracle's pins catch plausible mistakes: each case plants one mistake in
 a copy of the oracle's C source (on the CPU, in a temporary directory),
 builds it, points the oracle at it and runs the pins that should catch it.
-Every planted mistake must make at least one of those pins fail. The real
-oracle is untouched and reloaded afterwards."""
+Every planted mistake must make at least one of those pins fail. The verify
+block worked by hand under tests/golden/ must also catch, on its own, every
+planted mistake in the parts it exercises (head, survival, cuts without exact
+ties, packing, argmax ties, acceptance, bonus). The real oracle is untouched
+and reloaded afterwards."""
 import os
 import subprocess
 
 import pytest
 
 import oracle
+import test_golden as golden
 import test_oracle_pins as pins
 
 SRC = os.path.join(os.path.dirname(oracle.__file__), "dspark_oracle.c")
@@ -78,6 +82,12 @@ MUTATIONS = [
 ]
 
 
+# planted mistakes the hand-worked verify block alone must catch
+WORKED_CATCHES = ["temperature_on_dot_only", "sign_flip_in_sigmoid", "wrong_hidden_stride",
+                  "survival_shifted_by_one", "budget_ascending", "compact_drops_root_row",
+                  "argmax_last_of_ties", "accept_without_cap", "bonus_from_next_row"]
+
+
 def _pin_callables(names):
     out = []
     for n in names:
@@ -104,8 +114,7 @@ def restore_oracle():
     oracle.LIB = lib_path
 
 
-@pytest.mark.parametrize("name,orig,bad,catchers", MUTATIONS, ids=[m[0] for m in MUTATIONS])
-def test_pins_catch_planted_mistake(name, orig, bad, catchers, tmp_path, restore_oracle):
+def _load_mutant(name, orig, bad, tmp_path):
     src = open(SRC).read()
     assert src.count(orig) == 1, f"mutation anchor for {name} not unique in the oracle"
     mutated = tmp_path / "oracle_mut.c"
@@ -115,6 +124,11 @@ def test_pins_catch_planted_mistake(name, orig, bad, catchers, tmp_path, restore
                     "-fno-fast-math", "-o", str(lib), str(mutated), "-lm"], check=True)
     oracle._lib = None
     oracle.LIB = str(lib)
+
+
+@pytest.mark.parametrize("name,orig,bad,catchers", MUTATIONS, ids=[m[0] for m in MUTATIONS])
+def test_pins_catch_planted_mistake(name, orig, bad, catchers, tmp_path, restore_oracle):
+    _load_mutant(name, orig, bad, tmp_path)
     caught = []
     for f, kw in _pin_callables(catchers):
         try:
@@ -122,3 +136,11 @@ def test_pins_catch_planted_mistake(name, orig, bad, catchers, tmp_path, restore
         except (AssertionError, oracle.OracleError) as e:
             caught.append((f.__name__, type(e).__name__))
     assert caught, f"no pin caught the planted mistake {name}"
+
+
+@pytest.mark.parametrize("name", WORKED_CATCHES)
+def test_worked_block_catches_planted_mistake(name, tmp_path, restore_oracle):
+    orig, bad = next((m[1], m[2]) for m in MUTATIONS if m[0] == name)
+    _load_mutant(name, orig, bad, tmp_path)
+    with pytest.raises((AssertionError, oracle.OracleError)):
+        golden.test_worked_block_oracle()
