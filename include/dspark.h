@@ -220,7 +220,11 @@ dspark_status dspark_cost_cutoff(const float *table, int n, const int32_t *load,
  * is read directly. Only packed rows are read. cu_seqlens [B+1] and
  * tokens [B, gamma+1] int32 inputs; packed_argmax [B*(gamma+1)], accepted
  * and bonus [B] int32 outputs. ws: scratch of at least
- * dspark_workspace_bytes(B, gamma, V) bytes, 16-byte aligned.
+ * dspark_workspace_bytes(B, gamma, V) bytes, 16-byte aligned, zero-filled
+ * before its first use (dspark_workspace_init): up to 4096 requests the call
+ * counts each request's streamed rows on a per-request counter at bytes
+ * [256 + 32 KiB, 256 + 64 KiB) of ws, which it returns to zero on completion.
+ * Calls that share a workspace must not overlap in time.
  */
 dspark_status dspark_accept(const dspark_bf16 *logits, const int32_t *packed_src_row,
                             const int32_t *cu_seqlens, const int32_t *tokens, int B, int gamma,
