@@ -102,7 +102,11 @@ def test_schedule_stage(name, surv):
 
 # --------------------------------------------------------------- compact
 
-@pytest.mark.parametrize("B,g", [(4, 8), (256, 16), (1500, 3), (1, 1), (3, 64)])
+# up to 4096 requests and 65536 positions one thread per position, beyond
+# that one workgroup: (4096, 15) is exactly at the position limit, (5000, 2)
+# and (300, 256) beyond one limit each
+@pytest.mark.parametrize("B,g", [(4, 8), (256, 16), (1500, 3), (1, 1), (3, 64), (4096, 15),
+                                 (5000, 2), (300, 256)])
 def test_compact_stage(B, g):
     rng = np.random.default_rng(B * 31 + g)
     L = rng.integers(0, g + 1, B).astype(np.int32)
