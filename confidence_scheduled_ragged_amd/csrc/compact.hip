@@ -56,62 +56,6 @@ __global__ __launch_bounds__(kCompactThreads) void compact_kernel(
 // blockIdx.y strides over packed rows, blockIdx.x * blockDim over a row's
 // elements; each thread has four loads in flight before it stores. A source
 // row outside [0, cap) leaves its packed row untouched.
-// The same outputs with one thread per verify-block position (b, j), for
-// B <= kWideMaxB requests and B*(gamma+1) <= kWideMaxPositions. Every
-// workgroup loads all B lengths (up to kWidePer per thread, all issued before
-// any is used) and scans them in LDS; the thread then writes its position's
-// packed token and source row when j <= L_b. Its token load is issued first,
-// as it does not depend on the lengths. Two memory round trips in all,
-// instead of one workgroup walking every position in turn.
-constexpr int kWideThreads = 256;
-constexpr int kWidePer = 16;
-constexpr int kWideMaxB = kWideThreads * kWidePer;
-constexpr int kWideMaxPositions = 65536;
-
-__global__ __launch_bounds__(kWideThreads) void compact_wide_kernel(
-    const int32_t *__restrict__ lengths, const int32_t *__restrict__ tokens, int B, int gamma,
-    int32_t *__restrict__ cu, int32_t *__restrict__ ptok, int32_t *__restrict__ psrc) {
-    __shared__ int cu_s[kWideMaxB + 1];
-    __shared__ int scan_lds[17];
-    const int g1 = gamma + 1;
-    const int q = blockIdx.x * blockDim.x + threadIdx.x;
-    const bool inq = q < B * g1;
-    const int tok = inq ? tokens[q] : 0;
-    int n[kWidePer];
-#pragma unroll
-    for (int k = 0; k < kWidePer; ++k) {
-        const int b = k * kWideThreads + threadIdx.x;
-        n[k] = b < B ? lengths[b] : -1;
-    }
-    int carry = 0;
-#pragma unroll
-    for (int k = 0; k < kWidePer; ++k) {
-        if (k * kWideThreads >= B) break;  // uniform across the block
-        const int b = k * kWideThreads + threadIdx.x;
-        int x = 0;
-        if (b < B) {
-            const int L = n[k] < 0 ? 0 : (n[k] > gamma ? gamma : n[k]);
-            x = L + 1;
-        }
-        int tot;
-        const int st = carry + block_excl_scan(x, &tot, scan_lds);
-        if (b < B) cu_s[b] = st;
-        carry += tot;
-    }
-    if (threadIdx.x == 0) cu_s[B] = carry;
-    __syncthreads();
-    if (inq) {
-        const int b = q / g1, j = q - b * g1;
-        const int start = cu_s[b];
-        if (j < cu_s[b + 1] - start) {
-            ptok[start + j] = tok;
-            psrc[start + j] = q;
-        }
-        if (j == 0) cu[b + 1] = cu_s[b + 1];
-        if (q == 0) cu[0] = 0;
-    }
-}
-
 template <typename T>
 __global__ __launch_bounds__(256) void gather_rows_kernel(const T *__restrict__ src,
                                                           const int32_t *__restrict__ psrc,
@@ -158,15 +102,8 @@ static void launch_gather_typed(const void *src, const int32_t *psrc, const int3
 
 hipError_t launch_compact(const int32_t *lengths, const int32_t *tokens, int B, int gamma,
                           int32_t *cu, int32_t *ptok, int32_t *psrc, hipStream_t s) {
-    const int64_t positions = (int64_t)B * (gamma + 1);
-    if (B <= kWideMaxB && positions <= kWideMaxPositions) {
-        const int grid = (int)((positions + kWideThreads - 1) / kWideThreads);
-        hipLaunchKernelGGL(compact_wide_kernel, dim3(grid), dim3(kWideThreads), 0, s, lengths,
-                           tokens, B, gamma, cu, ptok, psrc);
-    } else {
-        hipLaunchKernelGGL(compact_kernel, dim3(1), dim3(kCompactThreads), 0, s, lengths, tokens,
-                           B, gamma, cu, ptok, psrc);
-    }
+    hipLaunchKernelGGL(compact_kernel, dim3(1), dim3(kCompactThreads), 0, s, lengths, tokens, B,
+                       gamma, cu, ptok, psrc);
     return hipGetLastError();
 }
 
