@@ -572,9 +572,12 @@ def main():
     ap.add_argument("--rotation", type=int, default=8)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra-arms", action="store_true")
-    ap.add_argument("--profile-budget", action="store_true",
-                    help="time only the budget workload (d=7168 V=129280 T=768), for a kernel "
-                         "trace of that workload; prints its arm summary instead of the JSON line")
+    ap.add_argument("--profile-budget", nargs="?", const="budget", default=None,
+                    choices=["budget", "mixed_budget", "mixed_combined"],
+                    help="time only one batch-wide-pick workload (default: the budget workload, "
+                         "d=7168 V=129280 T=768; or the mixed workload's budget or combined "
+                         "arm), for a kernel trace of it; prints its arm summary instead of the "
+                         "JSON line")
     ap.add_argument("--no-all-cores", action="store_true",
                     help="skip the oracle timing on all host cores")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -594,7 +597,7 @@ def main():
     dev = torch.device("cuda:0")
     dspark.lib()
     if args.profile_budget:
-        cfg4 = CONFIGS["budget"]
+        cfg4 = CONFIGS[args.profile_budget]
         p4 = make_params(cfg4)
         slots4 = [make_step(cfg4, i, device=dev, params=p4) for i in range(args.rotation)]
         outs4 = [dspark.alloc_step_outputs(cfg4.B, cfg4.gamma, dev) for _ in slots4]
