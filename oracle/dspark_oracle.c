@@ -17,9 +17,10 @@
  *
  * Arithmetic: every bf16 and fp32 input is widened exactly to double and all
  * arithmetic is done in double, in the plain order stated in each function.
- * The one decision that turns floating point into integers, the cut, is taken
- * at binary32 precision (see decide_binary32). Readings of points the pages
- * leave open are stated where they are used.
+ * The cut, the one decision that turns floating point into integers, compares
+ * and ranks these double survival values as they are; the pages fix no other
+ * precision for it. Readings of points the pages leave open are stated where
+ * they are used.
  */
 #include <math.h>
 #include <stdint.h>
@@ -112,15 +113,6 @@ int oracle_survival(const double *conf, int B, int gamma, double *surv)
     return ORACLE_OK;
 }
 
-/* The cut turns floating-point survival values into integer lengths. The
- * pages fix no precision for that decision, so it is taken at the precision
- * the GPU kernel decides in, IEEE binary32: the fp64 survival value is rounded
- * once to binary32 (round to nearest even) and compared exactly. */
-static double decide_binary32(double s)
-{
-    return (double)(float)s;
-}
-
 /*
  * Step 3, per-request cut [P1, "DSpark: a sequential head and a verify
  * budget" and "The confidence scheduler and verify modes"]: walk down the
@@ -130,8 +122,8 @@ static double decide_binary32(double s)
  * The verify length is the number of kept drafts,
  *     L_b = #{k in 1..gamma : S_k >= c_b},
  * which equals the walk's stopping point because S is non-increasing. A NaN
- * cutoff keeps nothing (every comparison is false). S_k is compared at
- * binary32 precision (decide_binary32).
+ * cutoff keeps nothing (every comparison is false). The cutoff is widened
+ * exactly to double and compared with the double S_k.
  */
 int oracle_cut_threshold(const double *surv, const float *cutoff, int B, int gamma,
                          int32_t *lengths)
@@ -145,7 +137,7 @@ int oracle_cut_threshold(const double *surv, const float *cutoff, int B, int gam
             double s = surv[(size_t)b * gamma + (k - 1)];
             if (!isfinite(s))
                 return ORACLE_ERR_NONFINITE;
-            if (decide_binary32(s) >= c)
+            if (s >= c)
                 n += 1;
         }
         lengths[b] = n;
@@ -180,8 +172,8 @@ static int oracle_rank_cmp(const void *pa, const void *pb)
  * T counts drafted positions (root rows are always verified and are not
  * counted); T larger than B*gamma takes every position; equal survival values
  * are ranked by lower request, then lower position. L_b is the number of
- * request b's positions among the T picked. Survival values are ranked at
- * binary32 precision (decide_binary32), so values equal in binary32 tie.
+ * request b's positions among the T picked. The double survival values are
+ * ranked as they are: only exactly equal values tie.
  */
 int oracle_cut_budget(const double *surv, int B, int gamma, long long budget,
                       int32_t *lengths)
@@ -200,7 +192,7 @@ int oracle_cut_budget(const double *surv, int B, int gamma, long long budget,
             free(items);
             return ORACLE_ERR_NONFINITE;
         }
-        items[f].s = decide_binary32(surv[f]);
+        items[f].s = surv[f];
         items[f].flat = f;
     }
     qsort(items, (size_t)n, sizeof *items, oracle_rank_cmp);
@@ -216,7 +208,7 @@ int oracle_cut_budget(const double *surv, int B, int gamma, long long budget,
  * Step 3, threshold and budget together [P1, "The confidence scheduler and
  * verify modes" (per-request marginal cost) with "Zero-overhead scheduling and
  * kernels" (batch-wide top-k budget)]. Reading: a drafted position is eligible
- * when it passes its request's cutoff, S_k >= c_b (at binary32, as in
+ * when it passes its request's cutoff, S_k >= c_b (in double, as in
  * oracle_cut_threshold), and the batch then verifies the T eligible positions
  * with the largest survival (ties by lower request, then lower position), or
  * every eligible position when there are at most T. Eligibility is a prefix of
@@ -240,7 +232,7 @@ int oracle_cut_combined(const double *surv, const float *cutoff, int B, int gamm
             free(items);
             return ORACLE_ERR_NONFINITE;
         }
-        double s = decide_binary32(surv[f]);
+        double s = surv[f];
         if (s >= (double)cutoff[f / gamma]) {
             items[m].s = s;
             items[m].flat = f;

@@ -36,6 +36,16 @@ class OracleStep:
     bonus: np.ndarray
     ambiguous_positions: int
     ambiguous_requests: np.ndarray
+    # valid verify lengths per request: [lo_b, hi_b] (lo == hi == L_b unless
+    # request b holds an ambiguous position)
+    len_lo: np.ndarray = None
+    len_hi: np.ndarray = None
+    # the batch total of lengths every valid schedule has (budget cut), or -1
+    len_total: int = -1
+    # the batch total no valid schedule exceeds (combined cut), or -1
+    len_cap: int = -1
+    # oracle argmax of every row 0..gamma of each ambiguous request
+    amb_amax: Dict[int, np.ndarray] = field(default_factory=dict)
 
 
 @dataclass
@@ -57,58 +67,127 @@ def snapshot(s) -> HostStep:
                     s.host("cutoff"), s.budget, s.host("tokens"), s.plant)
 
 
-def oracle_front(h: HostStep):
-    """Oracle steps 1-4: returns (conf, surv, lengths, cu, ptok, psrc, n_amb, amb_req)."""
+@dataclass
+class Front:
+    """Oracle steps 1-4 and the band of valid lengths around its cut."""
+    conf: np.ndarray
+    surv: np.ndarray
+    lengths: np.ndarray
+    cu: np.ndarray
+    ptok: np.ndarray
+    psrc: np.ndarray
+    ambiguous_positions: int
+    ambiguous_requests: np.ndarray
+    len_lo: np.ndarray
+    len_hi: np.ndarray
+    len_total: int
+    len_cap: int
+    gamma: int
+
+    @property
+    def total(self) -> int:
+        return int(self.cu[-1])
+
+    def packed_rows(self) -> np.ndarray:
+        """Dense logit rows the oracle's own schedule selects."""
+        return self.psrc[: self.total]
+
+    def ambiguous_rows(self) -> np.ndarray:
+        """Every dense row (0..gamma) of each ambiguous request."""
+        g1 = self.gamma + 1
+        return np.concatenate([b * g1 + np.arange(g1) for b in self.ambiguous_requests]
+                              + [np.zeros(0, np.int64)]).astype(np.int64)
+
+
+def _above(surv: np.ndarray, ref: np.ndarray) -> np.ndarray:
+    """Per request: positions certainly above `ref` and possibly at or above it."""
+    d = surv - ref
+    return (d > BAND).sum(axis=1), (d >= -BAND).sum(axis=1)
+
+
+def oracle_front(h: HostStep) -> Front:
     _, conf = oracle.confidence(h.hidden, h.w, h.bias, h.temps)
     surv = oracle.survival(conf)
+    B = surv.shape[0]
+    total_fixed, cap = -1, -1
     if h.cfg.mode == "threshold":
         L = oracle.cut_threshold(surv, h.cutoff)
-        amb = np.abs(surv - h.cutoff.astype(np.float64)[:, None]) <= BAND
+        c = h.cutoff.astype(np.float64)[:, None]
+        amb = np.abs(surv - c) <= BAND
+        lo, hi = _above(surv, c)
     elif h.cfg.mode == "combined":
         L = oracle.cut_combined(surv, h.cutoff, h.budget)
         c = h.cutoff.astype(np.float64)[:, None]
         amb = np.abs(surv - c) <= BAND
+        lo, hi = _above(surv, c)
+        cap = int(h.budget)
         elig = np.sort(surv[surv >= c])[::-1]
         t = min(h.budget, elig.size)
         if 0 < t < elig.size:
             tau = elig[t - 1]
             near_cut = amb.copy()
             amb |= np.abs(surv - tau) <= BAND
+            lo = np.minimum(lo, _above(surv, np.full_like(c, tau))[0])
             # a position that may or may not pass its cutoff and would rank
             # inside the budget can move the budget's last pick to any request
             if np.any(near_cut & (surv >= tau - BAND)):
                 amb[:] = True
+                lo = np.zeros_like(lo)
     elif h.cfg.mode == "static":
         L = oracle.cut_static(h.cfg.B, h.cfg.gamma)
         amb = np.zeros_like(surv, dtype=bool)
+        lo = hi = L
     else:
         L = oracle.cut_budget(surv, h.budget)
         n = surv.size
         t = min(h.budget, n)
+        total_fixed = t
         if 0 < t < n:
             tau = np.sort(surv.ravel())[::-1][t - 1]
             amb = np.abs(surv - tau) <= BAND
+            lo, hi = _above(surv, np.full((B, 1), tau))
         else:
             amb = np.zeros_like(surv, dtype=bool)
+            lo = hi = L
+    amb_req = np.nonzero(amb.any(axis=1))[0]
+    lo = np.where(amb.any(axis=1), lo, L).astype(np.int64)
+    hi = np.where(amb.any(axis=1), hi, L).astype(np.int64)
+    assert np.all(lo <= L) and np.all(L <= hi)
     cu, ptok, psrc = oracle.compact(L, h.tokens)
-    return conf, surv, L, cu, ptok, psrc, int(amb.sum()), np.nonzero(amb.any(axis=1))[0]
+    return Front(conf, surv, L, cu, ptok, psrc, int(amb.sum()), amb_req, lo, hi,
+                 total_fixed, cap, int(h.cfg.gamma))
 
 
-def oracle_back(h: HostStep, front, rows: np.ndarray) -> OracleStep:
-    """Oracle steps 5-6 on the packed rows the oracle itself selected."""
-    conf, surv, L, cu, ptok, psrc, n_amb, amb_req = front
+def oracle_back(h: HostStep, front: Front, rows: np.ndarray,
+                amb_rows: np.ndarray = None) -> OracleStep:
+    """Oracle steps 5-6 on the packed rows the oracle itself selected.
+    `amb_rows` ([n_ambiguous_requests * (gamma+1), V], optional) are every row
+    of the ambiguous requests, in the order of `front.ambiguous_rows()`."""
+    f = front
     amax = oracle.argmax_rows(rows)
-    acc, bon = oracle.accept(cu, h.tokens, amax)
-    return OracleStep(conf, surv, L, cu, ptok, psrc, amax, acc, bon, n_amb, amb_req)
+    acc, bon = oracle.accept(f.cu, h.tokens, amax)
+    amb_amax = {}
+    if amb_rows is not None and len(f.ambiguous_requests):
+        full = oracle.argmax_rows(amb_rows).reshape(len(f.ambiguous_requests), f.gamma + 1)
+        amb_amax = {int(b): full[i] for i, b in enumerate(f.ambiguous_requests)}
+    return OracleStep(f.conf, f.surv, f.lengths, f.cu, f.ptok, f.psrc, amax, acc, bon,
+                      f.ambiguous_positions, f.ambiguous_requests, f.len_lo, f.len_hi,
+                      f.len_total, f.len_cap, amb_amax)
+
+
+def oracle_rows(s, front: Front):
+    """Host copies of the rows the oracle reads: its packed rows, then every row
+    of each ambiguous request."""
+    return s.host_rows(front.packed_rows()), s.host_rows(front.ambiguous_rows())
 
 
 def run_oracle(s) -> OracleStep:
     """The oracle's whole step on host copies of generated inputs. Only the
-    packed logit rows the oracle itself selects are copied to the host."""
+    packed logit rows the oracle itself selects (and every row of a request
+    holding an ambiguous position) are copied to the host."""
     h = snapshot(s)
     front = oracle_front(h)
-    total = int(front[3][-1])
-    return oracle_back(h, front, s.host_rows(front[5][:total]))
+    return oracle_back(h, front, *oracle_rows(s, front))
 
 
 @dataclass
@@ -153,17 +232,37 @@ def compare(g: Dict[str, np.ndarray], o: OracleStep, tokens: np.ndarray, ctx: st
         assert np.array_equal(g["accepted"], o.accepted), f"{ctx} accepted"
         assert np.array_equal(g["bonus"], o.bonus), f"{ctx} bonus"
     else:
-        g1 = tokens.shape[1]
+        # A flipped length must lie in the band of valid lengths, and the batch
+        # must keep the totals every valid schedule has.
+        for b in flips:
+            assert o.len_lo[b] <= gL[b] <= o.len_hi[b], \
+                f"{ctx} request {b}: gpu length {gL[b]} outside [{o.len_lo[b]}, {o.len_hi[b]}]"
+        if o.len_total >= 0:
+            assert int(gL.sum()) == o.len_total, f"{ctx} budget total {gL.sum()} != {o.len_total}"
+        if o.len_cap >= 0:
+            assert int(gL.sum()) <= o.len_cap, f"{ctx} combined total {gL.sum()} > {o.len_cap}"
         for b in range(B):
+            gs, n = int(gcu[b]), int(gL[b]) + 1
             if b in flips:
+                # the rows, acceptance and bonus follow from the oracle's own
+                # argmax of the request's rows, over the GPU's (valid) length
+                g1 = tokens.shape[1]
+                assert np.array_equal(g["packed_tokens"][gs:gs + n], tokens[b, :n]), ctx
+                assert np.array_equal(g["packed_src_row"][gs:gs + n], b * g1 + np.arange(n)), ctx
+                if b in o.amb_amax:
+                    full = o.amb_amax[b]
+                    assert np.array_equal(g["packed_argmax"][gs:gs + n], full[:n]), ctx
+                    a = 0
+                    while a < n - 1 and full[a] == tokens[b, a + 1]:
+                        a += 1
+                    assert g["accepted"][b] == a and g["bonus"][b] == full[a], \
+                        f"{ctx} request {b} accept/bonus on flipped length"
                 continue
-            gs, os_ = int(gcu[b]), int(o.cu[b])
-            n = int(o.lengths[b]) + 1
+            os_ = int(o.cu[b])
             assert np.array_equal(g["packed_tokens"][gs:gs + n], o.ptok[os_:os_ + n]), ctx
             assert np.array_equal(g["packed_src_row"][gs:gs + n], o.psrc[os_:os_ + n]), ctx
             assert np.array_equal(g["packed_argmax"][gs:gs + n], o.amax[os_:os_ + n]), ctx
             assert g["accepted"][b] == o.accepted[b] and g["bonus"][b] == o.bonus[b], ctx
-        del g1
     return rep
 
 

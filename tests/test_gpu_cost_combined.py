@@ -15,7 +15,7 @@ import torch
 import __graft_entry__  # noqa: F401
 import confidence_scheduled_ragged_amd as dspark
 import oracle
-from parity_utils import compare, oracle_back, oracle_front, snapshot
+from parity_utils import compare, oracle_back, oracle_front, oracle_rows, snapshot
 from synth import CONFIGS, make_step
 
 pytestmark = pytest.mark.gpu
@@ -62,8 +62,7 @@ def _run(cfg, steps, s_cutoff=None):
         g = {k: v.cpu().numpy() for k, v in out.items()}
         h = snapshot(s)
         front = oracle_front(h)
-        rows = s.host_rows(front[5][: int(front[3][-1])])
-        o = oracle_back(h, front, rows)
+        o = oracle_back(h, front, *oracle_rows(s, front))
         compare(g, o, h.tokens, ctx=f"{cfg.name} step {step}")
 
 
@@ -105,7 +104,7 @@ def test_cost_table_drives_the_step():
         h = snapshot(s)
         h.cutoff = oracle.cost_cutoff(table, load, cfg.B)
         front = oracle_front(h)
-        o = oracle_back(h, front, s.host_rows(front[5][: int(front[3][-1])]))
+        o = oracle_back(h, front, *oracle_rows(s, front))
         compare(g, o, h.tokens, ctx=f"cost table load {load}")
         if prev is not None:
             assert np.all(o.lengths <= prev)

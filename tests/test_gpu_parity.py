@@ -14,7 +14,8 @@ import torch
 import __graft_entry__  # noqa: F401
 import confidence_scheduled_ragged_amd as dspark
 import oracle
-from parity_utils import compare, oracle_back, oracle_front, planted_accept_pin, snapshot
+from parity_utils import (compare, oracle_back, oracle_front, oracle_rows, planted_accept_pin,
+                          snapshot)
 from synth import CONFIGS, bf16_bits_to_f32, make_step, rne_bf16
 
 pytestmark = pytest.mark.gpu
@@ -244,11 +245,11 @@ def _run_workload(cfg, steps, tag):
             g = _gpu_step(s)
             h = snapshot(s)
             front = oracle_front(h)
-            rows = s.host_rows(front[5][: int(front[3][-1])])
+            rows = oracle_rows(s, front)
             del s
 
             def job(h=h, front=front, rows=rows, g=g, step=step):
-                o = oracle_back(h, front, rows)
+                o = oracle_back(h, front, *rows)
                 rep = compare(g, o, h.tokens, ctx=f"{tag} step {step}")
                 planted_accept_pin(h, o)
                 return rep

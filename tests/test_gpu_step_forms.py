@@ -15,7 +15,7 @@ import torch
 
 import __graft_entry__  # noqa: F401
 import confidence_scheduled_ragged_amd as dspark
-from parity_utils import compare, oracle_back, oracle_front, snapshot
+from parity_utils import compare, oracle_back, oracle_front, oracle_rows, snapshot
 from synth import CONFIGS, make_step
 
 pytestmark = pytest.mark.gpu
@@ -110,8 +110,8 @@ def test_both_forms_match_the_oracle_and_each_other(name, monkeypatch):
             assert np.array_equal(L.cpu().numpy(), one["lengths"]), f"{name} step {step}"
         h = snapshot(s)
         front = oracle_front(h)
-        rows = s.host_rows(front[5][: int(front[3][-1])])
-        compare(one, oracle_back(h, front, rows), h.tokens, ctx=f"{name} step {step}")
+        compare(one, oracle_back(h, front, *oracle_rows(s, front)), h.tokens,
+                ctx=f"{name} step {step}")
 
 
 def test_forms_alternate_on_one_workspace(monkeypatch):

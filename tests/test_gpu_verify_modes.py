@@ -95,11 +95,12 @@ def test_cap_accept_matches_oracle_and_compact(name, steps):
         # against the oracle's own cut, full-block argmax and cap
         h = snapshot(s)
         front = oracle_front(h)
-        oL, amb_req = front[2], front[7]
+        oL, amb_req = front.lengths, front.ambiguous_requests
         o_acc, o_bon, o_full = oracle.cap_accept(oL, h.tokens, _oracle_full_argmax(s))
         assert np.array_equal(full, o_full)
         same = gL == oL
         assert np.all(same | np.isin(np.arange(cfg.B), amb_req)), "length flip off the band"
+        assert np.all((front.len_lo <= gL) & (gL <= front.len_hi)), "length outside the band"
         assert np.array_equal(acc[same], o_acc[same]) and np.array_equal(bon[same], o_bon[same])
         utils.append(oracle.utilization(o_acc, o_full))
         if same.all():

@@ -36,8 +36,8 @@ MUTATIONS = [
      "            surv[(size_t)b * gamma + (k - 1)] = s;\n            s = s * p;",
      ["test_survival_constant_closed_form"]),
     ("threshold_strict",
-     "if (decide_binary32(s) >= c)",
-     "if (decide_binary32(s) > c)",
+     "            if (s >= c)\n",
+     "            if (s > c)\n",
      ["test_threshold_special_cases", "test_threshold_constant_closed_form"]),
     ("budget_ties_to_higher_request",
      "    if (a->flat < b->flat) return -1;\n    if (a->flat > b->flat) return 1;",

@@ -186,15 +186,13 @@ def test_budget_brute_force(seed):
     B = int(rng.integers(1, 5))
     g = int(rng.integers(1, 9 if B <= 3 else 7))
     s = oracle.survival(rng.uniform(0.2, 1.0, (B, g)))
-    # The oracle ranks at binary32 precision, so the objective may differ from
-    # the fp64 brute force by at most the binary32 rounding of the values.
     for T in sorted({0, 1, int(rng.integers(0, B * g + 1)), B * g // 2, B * g, B * g + 3}):
         L = oracle.cut_budget(s, T)
         best, arg, nbest = _brute_force_budget(s, T)
         got = sum(s[b, :L[b]].sum() for b in range(B))
-        assert abs(got - best) <= 1e-6 * max(1, T)
+        assert abs(got - best) <= 1e-12
         assert L.sum() == min(T, B * g)
-        if nbest == 1 and len(np.unique(s.astype(np.float32))) == s.size:
+        if nbest == 1:
             assert tuple(L) == arg
 
 
@@ -216,14 +214,19 @@ def test_budget_hand_examples():
     assert list(oracle.cut_budget(s, 3)) == [2, 1]
 
 
-def test_cut_decides_at_binary32():
-    # 0.3 + 1e-12 and 0.3 - 1e-12 both round to binary32(0.3): both are kept
-    # against c = binary32(0.3), and they tie in the budget ranking.
+def test_cut_compares_double_values_as_they_are():
+    # The cut compares and ranks the double survival values themselves: values
+    # 1e-12 apart are distinct, so one is kept and one is not against a cutoff
+    # lying between them, and the larger wins a budget of one whatever its
+    # request. A cut rounded to any coarser precision would keep or tie both.
     c = np.float32(0.3)
     s = np.array([[float(c) + 1e-12, float(c) - 1e-12]])
-    assert oracle.cut_threshold(s, np.array([c]))[0] == 2
+    assert oracle.cut_threshold(s, np.array([c]))[0] == 1
     s2 = np.array([[float(c) - 1e-12], [float(c) + 1e-12]])
-    assert list(oracle.cut_budget(s2, 1)) == [1, 0]        # tie -> lower request
+    assert list(oracle.cut_budget(s2, 1)) == [0, 1]
+    s3 = np.array([[float(c)], [float(c)]])
+    assert list(oracle.cut_budget(s3, 1)) == [1, 0]        # exact tie -> lower request
+    assert list(oracle.cut_combined(s2, np.array([c, c]), 1)) == [0, 1]
 
 
 def test_budget_rejects_negative():
