@@ -125,8 +125,9 @@ def run_arm(cfg, slots, outs, ws, steps, warmup, dspark, torch, kernel_events=Fa
     nothing else on the stream, then the same `steps` calls again with a HIP
     event pair around each (the per-step times; an event record adds its own
     gap to the stream, so it stays out of the wall-time pass). With
-    kernel_events, the event pass goes through dspark_step_profiled, which
-    records a second pair of events around the dominant kernel."""
+    kernel_events, the event pass goes through dspark_step_ex, which records a
+    second pair of events around the dominant kernel. Afterwards the
+    workspace's give-up flag must read 0 (no bounded wait gave up)."""
     R = len(slots)
     kev = None
 
@@ -168,6 +169,10 @@ def run_arm(cfg, slots, outs, ws, steps, warmup, dspark, torch, kernel_events=Fa
     torch.cuda.synchronize()
     step_ms = [a.elapsed_time(b) for a, b in ev]
     kernel_ms = [a.elapsed_time(b) for a, b in kev] if kev else None
+    st = int(dspark.dspark_step_status(ws).item())
+    if st != 0:
+        raise RuntimeError(f"{cfg.name}: a bounded wait of the fused step gave up "
+                           f"(dspark_step_status = {st}); the timed outputs are undefined")
     rows = sum(totals[i % R] for i in range(steps))
     nbytes = sum(step_bytes(cfg, totals[i % R]) for i in range(steps))
     mean_ms = sum(step_ms) / steps
@@ -742,7 +747,7 @@ def main():
                      "kernel": "step_one_kernel (the whole step in one launch: confidence "
                                "GEMV, survival, cut, compaction outputs, root and draft-row "
                                "argmax, acceptance, bonus), timed live between HIP events "
-                               "recorded around its launch by dspark_step_profiled",
+                               "recorded around its launch by dspark_step_ex",
                      "achieved": k_gbs,
                      "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": k_gbs / HBM_PEAK_GBS,
@@ -751,7 +756,7 @@ def main():
                                                   if traffic else None),
                      "algorithmic_bytes_per_launch": r_k["kernel_bytes"],
                      "mean_launch_us": r_k["kernel_mean_ms"] * 1e3,
-                     "timing": "second pass of the same steps through dspark_step_profiled"},
+                     "timing": "second pass of the same steps through dspark_step_ex"},
         "step_roofline": {"bound": "hbm",
                           "kernel": "the whole dspark_step (one launch), events around the "
                                     "call",

@@ -57,7 +57,8 @@ def lib() -> ctypes.CDLL:
         L.dspark_gather_rows.argtypes = [P, P, P, I, I, LL, P, P]
         L.dspark_tier_select.argtypes = [P, I, I, P, I, ctypes.c_int32, P, P, P, P, P]
         L.dspark_cost_cutoff.argtypes = [P, I, P, I, P, P]
-        L.dspark_step_profiled.argtypes = L.dspark_step.argtypes + [P, P]
+        L.dspark_step_ex.argtypes = L.dspark_step.argtypes + [P, P, I, ctypes.c_ulonglong]
+        L.dspark_step_status.argtypes = [P, P, P]
         L.dspark_workspace_bytes.argtypes = [I, I, I]
         L.dspark_workspace_bytes.restype = S
         L.dspark_workspace_init.argtypes = [P, S, P]
@@ -66,7 +67,7 @@ def lib() -> ctypes.CDLL:
         for f in (L.dspark_confidence, L.dspark_schedule, L.dspark_compact, L.dspark_accept,
                   L.dspark_step, L.dspark_workspace_init, L.dspark_cap_accept,
                   L.dspark_gather_rows, L.dspark_tier_select, L.dspark_cost_cutoff,
-                  L.dspark_step_profiled):
+                  L.dspark_step_ex, L.dspark_step_status):
             f.restype = ctypes.c_int
         _lib = L
     return _lib
@@ -124,6 +125,12 @@ def dspark_workspace_init(ws: torch.Tensor) -> None:
 _WS: Dict[tuple, torch.Tensor] = {}
 
 
+def _ws_key(device) -> tuple:
+    device = torch.device(device)
+    idx = device.index if device.index is not None else torch.cuda.current_device()
+    return (device.type, idx)
+
+
 def workspace(B: int, gamma: int, V: int, device) -> torch.Tensor:
     """A zero-initialised workspace of the required size, cached per device.
     Calls sharing it must not overlap in time (one stream, or ordered)."""
@@ -131,7 +138,7 @@ def workspace(B: int, gamma: int, V: int, device) -> torch.Tensor:
     need = dspark_workspace_bytes(B, gamma, V)
     if need == 0:
         raise ValueError(f"invalid sizes B={B} gamma={gamma} V={V}")
-    key = (device.type, device.index)
+    key = _ws_key(device)
     ws = _WS.get(key)
     if ws is None or ws.numel() < need:
         ws = torch.empty(need, dtype=torch.uint8, device=device)
@@ -373,10 +380,12 @@ def _event_handle(ev):
 
 
 def dspark_step(hidden, w, bias, temps, tokens, logits, mode, cutoff=None, budget=0, out=None,
-                ws=None, events=None):
-    """Steps 1-6 in one call; returns the dict of output tensors. `events`, a
-    pair of timing events, selects dspark_step_profiled: they are recorded
-    around the step's dominant kernel."""
+                ws=None, events=None, launches=0, wait_ticks=0):
+    """Steps 1-6 in one call; returns the dict of output tensors. With any of
+    `events` (a pair of timing events, recorded around the step's dominant
+    kernel), `launches` (0 by size, 1 one launch where the cut allows it, 2 two
+    launches) or `wait_ticks` (bound of the one-launch wait, 100 MHz ticks; 0 is
+    the default) the call goes through dspark_step_ex."""
     B, g, d = hidden.shape
     V = logits.shape[-1]
     _need(hidden, "hidden", torch.bfloat16)
@@ -403,26 +412,43 @@ def dspark_step(hidden, w, bias, temps, tokens, logits, mode, cutoff=None, budge
         _ptr(out["lengths"]), _ptr(out["cu_seqlens"]), _ptr(out["packed_tokens"]),
         _ptr(out["packed_src_row"]), _ptr(out["packed_argmax"]), _ptr(out["accepted"]),
         _ptr(out["bonus"]), _ptr(ws), ws.numel(), _stream(dev))
-    if events is None:
+    if events is None and not launches and not wait_ticks:
         _ok("dspark_step", lib().dspark_step(*args))
     else:
-        _ok("dspark_step_profiled", lib().dspark_step_profiled(
-            *args, _event_handle(events[0]), _event_handle(events[1])))
+        ev = events if events is not None else (None, None)
+        _ok("dspark_step_ex", lib().dspark_step_ex(
+            *args, _event_handle(ev[0]), _event_handle(ev[1]), int(launches), int(wait_ticks)))
     return out
 
 
-def dspark_step_profiled(hidden, w, bias, temps, tokens, logits, mode, events, cutoff=None,
-                         budget=0, out=None, ws=None):
-    """dspark_step with a pair of timing events recorded around its dominant
-    kernel (the draft-row stream)."""
+def dspark_step_ex(hidden, w, bias, temps, tokens, logits, mode, cutoff=None, budget=0,
+                   out=None, ws=None, events=None, launches=0, wait_ticks=0):
+    """dspark_step with explicit controls: timing events around its dominant
+    kernel, the form (launches) and the bound of the one-launch wait."""
     return dspark_step(hidden, w, bias, temps, tokens, logits, mode, cutoff=cutoff,
-                       budget=budget, out=out, ws=ws, events=events)
+                       budget=budget, out=out, ws=ws, events=events, launches=launches,
+                       wait_ticks=wait_ticks)
+
+
+def dspark_step_status(ws=None, status=None, device=None):
+    """The fused step's give-up flag of a workspace, read and cleared on the
+    device: an int32 [1] tensor, 0 when no call since the last read gave up its
+    bounded wait. ws defaults to the binding's cached workspace of `device`."""
+    if ws is None:
+        ws = _WS.get(_ws_key(device if device is not None else "cuda"))
+        if ws is None:
+            raise ValueError("no workspace has been used on this device")
+    _need(ws, "ws", torch.uint8)
+    status = torch.empty(1, dtype=torch.int32, device=ws.device) if status is None else status
+    _need(status, "status", torch.int32, (1,))
+    _ok("dspark_step_status", lib().dspark_step_status(_ptr(ws), _ptr(status), _stream(ws.device)))
+    return status
 
 
 __all__ = ["DsparkError", "lib", "LIB_PATH", "dspark_status_string", "dspark_confidence", "dspark_schedule",
            "dspark_compact", "dspark_accept", "dspark_step", "dspark_cap_accept",
            "dspark_gather_rows", "dspark_tier_select", "dspark_cost_cutoff",
-           "dspark_step_profiled",
+           "dspark_step_ex", "dspark_step_status",
            "dspark_workspace_bytes",
            "dspark_workspace_init", "workspace", "alloc_step_outputs", "STEP_OUTPUTS",
            "DSPARK_CUT_THRESHOLD", "DSPARK_CUT_BUDGET", "DSPARK_CUT_STATIC",

@@ -31,6 +31,19 @@ __global__ __launch_bounds__(256) void fill_zero_kernel(u32x4 *p, size_t n16) {
         p[i] = u32x4{0u, 0u, 0u, 0u};
 }
 
+__global__ void step_status_kernel(unsigned *flag, int32_t *status) {
+    if (threadIdx.x == 0)
+        *status = (int32_t)__hip_atomic_exchange(flag, 0u, __ATOMIC_RELAXED,
+                                                 __HIP_MEMORY_SCOPE_AGENT);
+}
+
+hipError_t launch_step_status(void *ws, int32_t *status, hipStream_t s) {
+    unsigned *flag = reinterpret_cast<unsigned *>(static_cast<char *>(ws) + ws_ctrl_offset() +
+                                                  kCtrlTimedOutOffset);
+    hipLaunchKernelGGL(step_status_kernel, dim3(1), dim3(64), 0, s, flag, status);
+    return hipGetLastError();
+}
+
 hipError_t launch_fill_zero(void *ws, size_t bytes, hipStream_t s) {
     const size_t n16 = bytes / 16;
     if (n16 == 0) return hipSuccess;
@@ -224,14 +237,14 @@ DSPARK_API dspark_status dspark_cap_accept(const int32_t *packed_argmax_full,
 }
 
 static dspark_status step_impl(const dspark_bf16 *hidden, const dspark_bf16 *w, float bias,
-                                     const float *temps, const int32_t *tokens,
-                                     const dspark_bf16 *logits, int B, int gamma, int d, int V,
-                                     int mode, const float *cutoff, long long budget, float *conf,
-                                     float *survival, int32_t *lengths, int32_t *cu_seqlens,
-                                     int32_t *packed_tokens, int32_t *packed_src_row,
-                                     int32_t *packed_argmax, int32_t *accepted, int32_t *bonus,
-                                     void *ws, size_t ws_bytes, void *stream, void *ev_start,
-                                     void *ev_stop) {
+                               const float *temps, const int32_t *tokens,
+                               const dspark_bf16 *logits, int B, int gamma, int d, int V,
+                               int mode, const float *cutoff, long long budget, float *conf,
+                               float *survival, int32_t *lengths, int32_t *cu_seqlens,
+                               int32_t *packed_tokens, int32_t *packed_src_row,
+                               int32_t *packed_argmax, int32_t *accepted, int32_t *bonus,
+                               void *ws, size_t ws_bytes, void *stream, void *ev_start,
+                               void *ev_stop, int launches, unsigned long long wait_ticks) {
     if (!hidden || !w || !temps || !tokens || !logits || !lengths || !cu_seqlens ||
         !packed_tokens || !packed_src_row || !packed_argmax || !accepted || !bonus || !ws)
         return DSPARK_ERR_NULL;
@@ -241,6 +254,7 @@ static dspark_status step_impl(const dspark_bf16 *hidden, const dspark_bf16 *w, 
     if (!valid_mode(mode)) return DSPARK_ERR_ARG;
     if (needs_budget(mode) && budget < 0) return DSPARK_ERR_ARG;
     if (!std::isfinite(bias)) return DSPARK_ERR_ARG;
+    if (launches < 0 || launches > 2) return DSPARK_ERR_ARG;
     if (misaligned(hidden, 2) || misaligned(w, 2) || misaligned(temps, 4) ||
         misaligned(tokens, 4) || misaligned(logits, 2) || misaligned(cutoff, 4) ||
         misaligned(conf, 4) || misaligned(survival, 4) || misaligned(lengths, 4) ||
@@ -256,7 +270,8 @@ static dspark_status step_impl(const dspark_bf16 *hidden, const dspark_bf16 *w, 
     hipEvent_t es = static_cast<hipEvent_t>(ev_start), et = static_cast<hipEvent_t>(ev_stop);
     hipError_t e = launch_fused_step(hidden, w, bias, temps, tokens, logits, B, gamma, d, V, mode,
                                      cutoff, budget, cf, surv, lengths, cu_seqlens, packed_tokens,
-                                     packed_src_row, packed_argmax, accepted, bonus, ws, s, es, et);
+                                     packed_src_row, packed_argmax, accepted, bonus, ws, s, es, et,
+                                     launches, wait_ticks);
     if (e != hipErrorNotSupported) return launched(e);
     // sizes outside the fused kernels' limits: the same step through the stage kernels
     e = launch_confidence(hidden, w, bias, temps, B, gamma, d, cf, surv, s);
@@ -281,17 +296,24 @@ DSPARK_API dspark_status dspark_step(const dspark_bf16 *hidden, const dspark_bf1
                                      void *ws, size_t ws_bytes, void *stream) {
     return step_impl(hidden, w, bias, temps, tokens, logits, B, gamma, d, V, mode, cutoff, budget,
                      conf, survival, lengths, cu_seqlens, packed_tokens, packed_src_row,
-                     packed_argmax, accepted, bonus, ws, ws_bytes, stream, nullptr, nullptr);
+                     packed_argmax, accepted, bonus, ws, ws_bytes, stream, nullptr, nullptr, 0, 0);
 }
 
-DSPARK_API dspark_status dspark_step_profiled(
+DSPARK_API dspark_status dspark_step_ex(
     const dspark_bf16 *hidden, const dspark_bf16 *w, float bias, const float *temps,
     const int32_t *tokens, const dspark_bf16 *logits, int B, int gamma, int d, int V, int mode,
     const float *cutoff, long long budget, float *conf, float *survival, int32_t *lengths,
     int32_t *cu_seqlens, int32_t *packed_tokens, int32_t *packed_src_row, int32_t *packed_argmax,
     int32_t *accepted, int32_t *bonus, void *ws, size_t ws_bytes, void *stream, void *ev_start,
-    void *ev_stop) {
+    void *ev_stop, int launches, unsigned long long wait_ticks) {
     return step_impl(hidden, w, bias, temps, tokens, logits, B, gamma, d, V, mode, cutoff, budget,
                      conf, survival, lengths, cu_seqlens, packed_tokens, packed_src_row,
-                     packed_argmax, accepted, bonus, ws, ws_bytes, stream, ev_start, ev_stop);
+                     packed_argmax, accepted, bonus, ws, ws_bytes, stream, ev_start, ev_stop,
+                     launches, wait_ticks);
+}
+
+DSPARK_API dspark_status dspark_step_status(void *ws, int32_t *status, void *stream) {
+    if (!ws || !status) return DSPARK_ERR_NULL;
+    if (misaligned(ws, 16) || misaligned(status, 4)) return DSPARK_ERR_ALIGN;
+    return launched(launch_step_status(ws, status, as_stream(stream)));
 }

@@ -108,10 +108,6 @@ __device__ __forceinline__ int64_t sub_len(int64_t E, int64_t Wt) {
 // acnt:  uint64 [kMaxFusedB]     per-request arrival counters of dspark_accept
 //                                (zero between calls: each request's last
 //                                arriver resets its own)
-// pslot: uint64 [kPickSlots]     per-position score slots of the one-launch
-//                                step with a batch-wide pick: (1 << 32) | the
-//                                score's bits once written, zero between calls
-//                                (the picking workgroup clears what it read)
 // keys:  uint64 [kMaxWaves + B*(gamma+1)] argmax segment keys of packed rows
 // rkeys: uint64 [kMaxWaves + B]  segment keys of the root rows (fused step)
 // surv:  float [B*gamma]         survival scratch (when the caller passes none)
@@ -119,19 +115,19 @@ __device__ __forceinline__ int64_t sub_len(int64_t E, int64_t Wt) {
 constexpr int64_t kMaxWaves = 16384;  // bound on waves (or sub-chunks) per pass
 constexpr int kMaxFusedB = 4096;      // largest batch of the fused step
 constexpr size_t kCtrlBytes = 256;
-constexpr int kPickSlots = 4096;      // positions B*gamma of the one-launch batch-wide pick
 // Words of the ctrl region: at 0 the arrival counter of the request
 // workgroups (both forms of the fused step); on the next 128-byte line the
-// one-launch step's count of workgroups yet to leave once the lengths are
-// final, and its time-out flag. The counters are zero between calls.
+// one-launch step's go word (positive while the lengths are final and
+// workgroups are yet to leave, zero between calls); at 192 the sticky time-out
+// flag (set when a workgroup gave up its bounded wait; read and cleared by
+// dspark_step_status).
 constexpr size_t kCtrlGoOffset = 128;
 constexpr size_t kCtrlTimedOutOffset = 192;
 
 inline size_t ws_ctrl_offset() { return 0; }
 inline size_t ws_rcnt_offset() { return kCtrlBytes; }
 inline size_t ws_acnt_offset() { return kCtrlBytes + (size_t)8 * kMaxFusedB; }
-inline size_t ws_pslot_offset() { return kCtrlBytes + (size_t)16 * kMaxFusedB; }
-inline size_t ws_keys_offset() { return ws_pslot_offset() + (size_t)8 * kPickSlots; }
+inline size_t ws_keys_offset() { return kCtrlBytes + (size_t)16 * kMaxFusedB; }
 inline size_t ws_rkeys_offset(int64_t B, int64_t gamma) {
     return ws_keys_offset() + (size_t)8 * (size_t)(kMaxWaves + B * (gamma + 1));
 }
@@ -181,6 +177,9 @@ hipError_t launch_fused_step(const uint16_t *hidden, const uint16_t *w, float bi
                              long long budget, float *conf, float *surv, int32_t *lengths,
                              int32_t *cu, int32_t *ptok, int32_t *psrc, int32_t *pam,
                              int32_t *acc, int32_t *bonus, void *ws, hipStream_t s,
-                             hipEvent_t ev_start = nullptr, hipEvent_t ev_stop = nullptr);
+                             hipEvent_t ev_start, hipEvent_t ev_stop, int launches,
+                             unsigned long long wait_ticks);
+// Reads the fused step's sticky time-out flag of ws into *status and clears it.
+hipError_t launch_step_status(void *ws, int32_t *status, hipStream_t s);
 
 }  // namespace dspark

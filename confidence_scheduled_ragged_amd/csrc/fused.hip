@@ -37,7 +37,6 @@
 // (the schedule and packing fused around the verify) and "Background"
 // (greedy acceptance and bonus token).
 #include <atomic>
-#include <cstdlib>
 
 #include "argmax_dev.hpp"
 #include "conf_dev.hpp"
@@ -467,15 +466,25 @@ __global__ __launch_bounds__(kStreamThreads) void step_stream_kernel(StreamParam
 // final, all of them stream the draft rows. The only wait is for the lengths,
 // which only request workgroups write; they come first in the grid and never
 // wait before their lengths are out, and the grid is sized to be resident at
-// once, so they all run. The wait is bounded; a workgroup that gives up sets a
-// flag and leaves.
+// once, so they all run.
+//
+// The go word: the last request workgroup to finish adds the grid size G to
+// it once every length is at the coherence point, and every workgroup takes
+// one off exactly once, when it leaves. Before the add the word is at most
+// zero; after it, it stays positive until the last workgroup has left, and it
+// is zero again at the end of every call. Waiters go on when it is positive.
+// The wait is bounded: a workgroup that gives up sets the sticky time-out
+// flag, takes its one off and leaves (the outputs of that call are then
+// undefined). Each request workgroup also returns its requests' arrival
+// counters to zero before it counts itself done, so a call that gave up leaves
+// nothing behind that could disturb the next one.
 struct OneParams {
     FrontParams f;
     StreamParams s;
     unsigned *gemv_done;  // request workgroups done (zero between calls)
-    unsigned *go;         // set to the grid size once every length is final; each
-                          // workgroup takes one off as it exits (zero between calls)
-    unsigned *timed_out;  // set when a workgroup gave up waiting for the lengths
+    int *go;              // see above (zero between calls)
+    unsigned *timed_out;  // sticky: set when a workgroup gave up waiting for the lengths
+    unsigned long long wait_ticks;  // bound of the wait, in 100 MHz clock ticks
     int gemv_wgs, root_wgs;
     int64_t lead;         // draft slots more per early wave than per root wave
 };
@@ -515,7 +524,7 @@ struct SplitLayout {
     }
 };
 
-// Upper bound of the wait for the lengths in ticks of the 100 MHz constant
+// Default bound of the wait for the lengths in ticks of the 100 MHz constant
 // clock (1 s; the lengths normally follow the slowest GEMV by microseconds).
 constexpr unsigned long long kWaitTicks = 100000000ull;
 
@@ -538,11 +547,16 @@ __global__ __launch_bounds__(kFrontThreads) void step_one_kernel(OneParams q) {
     bool wait = true;
     if (wg < q.gemv_wgs) {
         for (int b = wg; b < B; b += q.gemv_wgs) {
+            // the request's arrival counter starts this call at zero (streaming
+            // waves only add to it after the go word)
+            if (tid == 0)
+                __hip_atomic_store(sp.arrivals + b, (uint64_t)0, __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
             front_request<kVecH, kOneGemvUnroll>(p, p.w, b, false, true, z_s, p_s, s_s);
             __syncthreads();
         }
-        // this workgroup's length stores are at the coherence point: count it;
-        // the last to count lets every workgroup go on
+        // this workgroup's length and counter stores are at the coherence
+        // point: count it; the last to count lets every workgroup go on
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
         if (tid == 0) {
@@ -551,7 +565,7 @@ __global__ __launch_bounds__(kFrontThreads) void step_one_kernel(OneParams q) {
                              (unsigned)(q.gemv_wgs - 1);
             if (last) {
                 __hip_atomic_store(q.gemv_done, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                __hip_atomic_store(q.go, (unsigned)G, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                __hip_atomic_fetch_add(q.go, G, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             }
             last_s = last;
         }
@@ -565,15 +579,17 @@ __global__ __launch_bounds__(kFrontThreads) void step_one_kernel(OneParams q) {
         if (tid == 0) {
             const unsigned long long t0 = wall_clock64();
             int ok = 1;
-            while (__hip_atomic_load(q.go, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0u) {
-                if (wall_clock64() - t0 > kWaitTicks) {
+            while (__hip_atomic_load(q.go, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) <= 0) {
+                if (wall_clock64() - t0 > q.wait_ticks) {
                     ok = 0;
                     break;
                 }
                 __builtin_amdgcn_s_sleep(2);
             }
-            if (!ok)
+            if (!ok) {
                 __hip_atomic_store(q.timed_out, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                __hip_atomic_fetch_sub(q.go, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
             ok_s = ok;
         }
         __syncthreads();
@@ -620,282 +636,8 @@ __global__ __launch_bounds__(kFrontThreads) void step_one_kernel(OneParams q) {
         if (e0 < e1)
             stream_draft_span<kVecV, kOneStreamUnroll>(sp, cu_s, Vv, s_mine, e0, e1, arrive);
     }
-    // every wave of this workgroup is past the wait
-    if (tid == 0) __hip_atomic_fetch_sub(q.go, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-// ----------------------------------------------------- one launch, any cut
-
-// The whole step in one grid for every cut, batch-wide picks included. Every
-// wave first computes the head for one hidden row of the batch (rows gw,
-// gw + W, ... for wave gw of W): all B*gamma rows are read at once, each by
-// one wave, so the head runs at the bandwidth of the whole chip instead of
-// behind one workgroup per request. A wave stores its row's score in a slot of
-// its own (score bits with a ready mark), with no counter. Workgroup 0 then
-// reads every slot until all are marked (the only reader; it clears them for
-// the next call), forms the survival curves, cuts (threshold, static, budget
-// or combined), writes every length through to the device coherence point and
-// raises the go word. Meanwhile the other workgroups stream the root rows
-// (verified whatever the cut). After the go word they scan the lengths, write
-// their schedule outputs and stream the draft rows in one contiguous
-// sub-chunk per wave; per-request arrival counters name the wave that
-// finishes each request, as in step_one_kernel. Workgroup 0 waits for scores
-// that every other wave writes before it waits for anything; the others wait
-// once, for the go word that only workgroup 0 writes, and the grid is sized to
-// be resident at once, so every wait ends. Both waits are bounded. The step
-// takes this form only on request: at B = 256 it measured slower than the
-// two launches (see the launch code).
-struct PickParams {
-    FrontParams f;
-    StreamParams s;
-    uint64_t *slots;      // [B*gamma] score slots (zero between calls)
-    unsigned *go;         // as in OneParams
-    unsigned *timed_out;  // as in OneParams
-};
-
-constexpr int kPickGemvUnroll = 16;  // 16-byte hidden loads in flight per lane: d <= 8192 in one batch
-constexpr int kPickChunk = 16;       // score slots of one request read together by the picker
-
-// z = w.h + bias of one hidden row by the calling wave. Each lane accumulates
-// its 16-byte slots in increasing order and the wave then sums the lanes, the
-// same order as request_logits, so both give the same bits. w_s: the head in
-// LDS (kVec) or global memory.
-template <bool kVec>
-__device__ __forceinline__ float row_logit(const uint16_t *__restrict__ h,
-                                           const uint16_t *__restrict__ w_s, float bias, int d) {
-    const int lane = threadIdx.x & (kWave - 1);
-    float acc = 0.0f;
-    if (kVec) {
-        const u32x4 *h4 = reinterpret_cast<const u32x4 *>(h);
-        const u32x4 *w4 = reinterpret_cast<const u32x4 *>(w_s);
-        const int nv = d >> 3;
-        for (int v0 = lane; v0 < nv; v0 += kPickGemvUnroll * kWave) {
-            u32x4 hv[kPickGemvUnroll];
-#pragma unroll
-            for (int u = 0; u < kPickGemvUnroll; ++u)
-                if (v0 + u * kWave < nv) hv[u] = __builtin_nontemporal_load(h4 + v0 + u * kWave);
-#pragma unroll
-            for (int u = 0; u < kPickGemvUnroll; ++u) {
-                if (v0 + u * kWave < nv) {
-                    const u32x4 wv = w4[v0 + u * kWave];
-#pragma unroll
-                    for (int c = 0; c < 4; ++c) {
-                        acc = fmaf(bf16_lo(hv[u][c]), bf16_lo(wv[c]), acc);
-                        acc = fmaf(bf16_hi(hv[u][c]), bf16_hi(wv[c]), acc);
-                    }
-                }
-            }
-        }
-    } else {
-        for (int k = lane; k < d; k += kWave) acc = fmaf(bf16_f32(h[k]), bf16_f32(w_s[k]), acc);
-    }
-    return wave_sum_f32(acc) + bias;
-}
-
-// Workgroup 0 of step_pick_kernel: every score, the survival curves (left in
-// sv) and the lengths (written through to the coherence point and into
-// len_s). sv and rk: LDS for B*gamma floats each (rk: the ranked values of a
-// combined cut). False when a score never came (bounded wait). *flag_s must
-// be zero on entry, behind a barrier. Nothing else is written to global
-// memory here; the score slots are cleared and the survival output written
-// after the lengths are out.
-__device__ __forceinline__ bool pick_lengths(const PickParams &q, float *sv, float *rk,
-                                             int *len_s, uint32_t *hist, uint32_t *sh,
-                                             int *scan_lds, int *flag_s) {
-    const FrontParams &p = q.f;
-    const int tid = threadIdx.x, bd = blockDim.x;
-    const int N = p.B * p.gamma, g = p.gamma;
-    const unsigned long long t0 = wall_clock64();
-    {
-        // thread b reads request b's score slots, up to kPickChunk at a time,
-        // every load issued before any is waited for; slots not yet marked are
-        // read again after a short sleep. The survival product follows in
-        // registers (the same sequential fp32 product as request_survival).
-        bool late = false;
-        for (int b = tid; b < p.B && !late; b += bd) {
-            float s = 1.0f;
-            for (int i0 = 0; i0 < g && !late; i0 += kPickChunk) {
-                const int n = g - i0 < kPickChunk ? g - i0 : kPickChunk;
-                const uint64_t *sl = q.slots + (size_t)b * g + i0;
-                float v[kPickChunk];
-                unsigned pending = (1u << n) - 1u;
-                while (pending) {
-                    uint64_t x[kPickChunk];
-#pragma unroll
-                    for (int j = 0; j < kPickChunk; ++j)
-                        x[j] = (pending >> j) & 1u ? __hip_atomic_load(sl + j, __ATOMIC_RELAXED,
-                                                                       __HIP_MEMORY_SCOPE_AGENT)
-                                                   : 0ull;
-#pragma unroll
-                    for (int j = 0; j < kPickChunk; ++j) {
-                        if (((pending >> j) & 1u) && (x[j] >> 32) == 1ull) {
-                            v[j] = __uint_as_float((uint32_t)x[j]);
-                            pending &= ~(1u << j);
-                        }
-                    }
-                    if (pending) {
-                        if (wall_clock64() - t0 > kWaitTicks) {
-                            late = true;
-                            break;
-                        }
-                        __builtin_amdgcn_s_sleep(2);
-                    }
-                }
-                if (late) break;
-#pragma unroll
-                for (int j = 0; j < kPickChunk; ++j) {
-                    if (j < n) {
-                        s = s * v[j];
-                        sv[(size_t)b * g + i0 + j] = s;
-                    }
-                }
-            }
-        }
-        if (late) *flag_s = 1;  // benign race: every writer stores 1
-        __syncthreads();
-        if (*flag_s) return false;
-        if (p.mode == DSPARK_CUT_THRESHOLD || p.mode == DSPARK_CUT_STATIC) {
-            for (int b = tid; b < p.B; b += bd)
-                len_s[b] = p.mode == DSPARK_CUT_STATIC ? g
-                                                       : threshold_length(sv + b * g, g, p.cutoff[b]);
-        } else {
-            // combined: a position below its request's cutoff ranks below every
-            // eligible one, and the budget is capped by the eligible count
-            const bool combined = p.mode == DSPARK_CUT_COMBINED;
-            int eligible = N;
-            float *ranked = sv;
-            if (combined) {
-                int n = 0;
-                for (int f = tid; f < N; f += bd) {
-                    const float x = sv[f];
-                    const bool ok = x >= p.cutoff[f / g];
-                    n += ok ? 1 : 0;
-                    rk[f] = ok ? x : -INFINITY;
-                }
-                block_excl_scan(n, &eligible, scan_lds);  // contains the barriers rk needs
-                ranked = rk;
-            }
-            const int t = p.t < eligible ? p.t : eligible;
-            if (t <= 0 || t >= N) {
-                for (int b = tid; b < p.B; b += bd) len_s[b] = t <= 0 ? 0 : g;
-            } else {
-                const BudgetCut cut = budget_select_runs<kFusedSelPer>(ranked, N, t, hist, sh);
-                budget_lengths(ranked, nullptr, p.B, g, cut, len_s, scan_lds);
-            }
-        }
-        __syncthreads();
-    }
-    for (int b = tid; b < p.B; b += bd)
-        __hip_atomic_store(p.lengths + b, len_s[b], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    return true;
-}
-
-template <bool kVecH, bool kVecV>
-__global__ __launch_bounds__(kFrontThreads) void step_pick_kernel(PickParams q) {
-    extern __shared__ __align__(16) uint16_t dyn_lds[];
-    __shared__ uint32_t hist[kSelHistWords], sh[kSelShWords];
-    __shared__ int scan_lds[17];
-    __shared__ int flag_s;
-    const FrontParams &p = q.f;
-    const StreamParams &sp = q.s;
-    const int tid = threadIdx.x, nw = blockDim.x / kWave, wave = tid / kWave;
-    const int wg = blockIdx.x, G = gridDim.x, B = p.B, g = p.gamma;
-    const int64_t W = (int64_t)G * nw, gw = (int64_t)wg * nw + wave;
-    const int64_t Vv = kVecV ? (p.V >> 3) : p.V;
-    const int64_t root_waves = W - nw;  // every workgroup but the picker's
-    const int N = B * g;
-    // LDS: [max(2d, 8N) bytes: the head, then the picker's survival and ranked
-    // values][len_s B][cu_s B+1]
-    const size_t head_bytes = (size_t)(kVecH ? 2 * p.d : 0) > (size_t)8 * N
-                                  ? (size_t)(kVecH ? 2 * p.d : 0)
-                                  : (size_t)8 * N;
-    int *len_s = reinterpret_cast<int *>(reinterpret_cast<char *>(dyn_lds) + ((head_bytes + 15) & ~(size_t)15));
-    int *cu_s = len_s + B;
-
-    // the head, one hidden row per wave: the row's first loads are issued in
-    // row_logit after w is staged (one round trip for the staging, overlapped
-    // by every other workgroup's rows)
-    const uint16_t *wp = p.w;
-    if (kVecH) {
-        stage_w(p.w, p.d, dyn_lds);
-        __syncthreads();
-        wp = dyn_lds;
-    }
-    for (int64_t r = gw; r < N; r += W) {
-        const float z = row_logit<kVecH>(p.hidden + (size_t)r * (size_t)p.d, wp, p.bias, p.d);
-        const int i = (int)(r % g);
-        const float pr = 1.0f / (1.0f + expf(-z / p.temps[i]));
-        if ((tid & (kWave - 1)) == 0) {
-            p.conf[r] = pr;
-            __hip_atomic_store(q.slots + r, (1ull << 32) | (uint64_t)__float_as_uint(pr),
-                               __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        }
-    }
-
-    if (wg == 0) {
-        if (tid == 0) flag_s = 0;
-        __syncthreads();  // w in LDS is no longer needed
-        float *sv = reinterpret_cast<float *>(dyn_lds);
-        const bool ok = pick_lengths(q, sv, sv + N, len_s, hist, sh, scan_lds, &flag_s);
-        if (!ok) {
-            if (tid == 0)
-                __hip_atomic_store(q.timed_out, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            return;
-        }
-        // every length is at the coherence point: let the grid go on
-        __builtin_amdgcn_s_waitcnt(0);
-        __syncthreads();
-        if (tid == 0) __hip_atomic_store(q.go, (unsigned)G, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        // then the survival output, and the score slots cleared for the next call
-        for (int f = tid; f < N; f += blockDim.x) {
-            p.surv[f] = sv[f];
-            __hip_atomic_store(q.slots + f, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        }
-    } else {
-        front_root_rows<kVecV, kOneRootUnroll, true>(p, gw - nw, root_waves);
-        if (tid == 0) {
-            const unsigned long long t0 = wall_clock64();
-            int ok = 1;
-            while (__hip_atomic_load(q.go, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0u) {
-                if (wall_clock64() - t0 > kWaitTicks) {
-                    ok = 0;
-                    break;
-                }
-                __builtin_amdgcn_s_sleep(2);
-            }
-            if (!ok)
-                __hip_atomic_store(q.timed_out, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            flag_s = ok;
-        }
-        __syncthreads();
-        if (!flag_s) return;
-    }
-
-    // every length is final: the schedule in LDS and this workgroup's outputs
-    lengths_to_lds<true>(sp, len_s, cu_s, scan_lds);
-    write_schedule(sp, len_s, cu_s, wg, G);
-    const SplitLayout lay((int64_t)(cu_s[B] - B) * Vv, 0, W, 0);
-    const int64_t Kr = sub_len((int64_t)B * Vv, root_waves);
-    auto arrive = [&](int b, int64_t n) {
-        if (!arrive_last(sp.arrivals + b, n, (int64_t)(len_s[b] + 1) * Vv)) return;
-        const int start = cu_s[b];
-        const int dstart = start - b;  // first draft row of request b
-        wave_accept_rows(
-            [&](int j) {
-                if (j == 0) return row_argmax<true>(sp.rkeys, b, Vv, Kr);
-                const int64_t r = dstart + j - 1;
-                return segment_keys_argmax<true>(sp.keys, r, lay.sub(r * Vv),
-                                                 lay.sub((r + 1) * Vv - 1));
-            },
-            len_s[b] + 1, sp.gamma, sp.tokens + (size_t)b * (sp.gamma + 1), sp.pam + start,
-            sp.acc + b, sp.bonus + b);
-    };
-    if (wg > 0) root_segments((int64_t)B * Vv, Kr, Vv, gw - nw, root_waves, arrive);
-    int64_t e0, e1;
-    lay.span(gw, &e0, &e1);
-    if (e0 < e1) stream_draft_span<kVecV, kOneStreamUnroll>(sp, cu_s, Vv, gw, e0, e1, arrive);
-    // every wave of this workgroup is past the wait
-    if (tid == 0) __hip_atomic_fetch_sub(q.go, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    // every wave of this workgroup is past the wait: it leaves
+    if (tid == 0) __hip_atomic_fetch_sub(q.go, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // ----------------------------------------------------------------- launch
@@ -986,62 +728,14 @@ static hipError_t launch_one_v(const OneParams &q, int grid, size_t lds, hipStre
     return e;
 }
 
-template <bool kVecH, bool kVecV>
-static int pick_capacity(size_t lds) {
-    // workgroups of step_pick_kernel resident at once for this LDS size,
-    // cached per device and 4 KiB LDS bucket
-    static std::atomic<int> cache[64][16];
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
-    const int bucket = (int)((lds + 4095) / 4096);
-    if (bucket >= 16) return 0;
-    int cap = cache[dev][bucket].load(std::memory_order_relaxed);
-    if (cap > 0) return cap;
-    int blocks = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, step_pick_kernel<kVecH, kVecV>,
-                                                     kFrontThreads, (size_t)bucket * 4096) !=
-            hipSuccess ||
-        blocks < 0)
-        blocks = 0;
-    cap = blocks * device_cu_count();
-    if (cap > 0) cache[dev][bucket].store(cap, std::memory_order_relaxed);
-    return cap;
-}
-
-// Launches step_pick_kernel when a grid of `want` workgroups (at least two)
-// fits on the device at once; *done tells whether it did.
-template <bool kVecH, bool kVecV>
-static hipError_t launch_pick_v(const PickParams &q, int want, size_t lds, hipStream_t s,
-                                hipEvent_t ev_start, hipEvent_t ev_stop, bool *done) {
-    *done = false;
-    const int cap = pick_capacity<kVecH, kVecV>(lds);
-    const int grid = want < cap ? want : cap;
-    if (grid < 2) return hipSuccess;
-    hipError_t e;
-    if (ev_start && (e = hipEventRecord(ev_start, s)) != hipSuccess) return e;
-    hipLaunchKernelGGL((step_pick_kernel<kVecH, kVecV>), dim3(grid), dim3(kFrontThreads), lds, s,
-                       q);
-    e = hipGetLastError();
-    if (e == hipSuccess && ev_stop) e = hipEventRecord(ev_stop, s);
-    *done = e == hipSuccess;
-    return e;
-}
-
-// The form the caller asked for with DSPARK_STEP_LAUNCHES in the environment
-// (1 or 2, e.g. to compare or test both), else 0: chosen by size.
-static int forced_launches() {
-    const char *v = getenv("DSPARK_STEP_LAUNCHES");
-    if (v == nullptr || v[0] == '\0' || v[1] != '\0') return 0;
-    return v[0] == '1' ? 1 : (v[0] == '2' ? 2 : 0);
-}
-
 hipError_t launch_fused_step(const uint16_t *hidden, const uint16_t *w, float bias,
                              const float *temps, const int32_t *tokens, const uint16_t *logits,
                              int B, int gamma, int d, int V, int mode, const float *cutoff,
                              long long budget, float *conf, float *surv, int32_t *lengths,
                              int32_t *cu, int32_t *ptok, int32_t *psrc, int32_t *pam,
                              int32_t *acc, int32_t *bonus, void *ws, hipStream_t s,
-                             hipEvent_t ev_start, hipEvent_t ev_stop) {
+                             hipEvent_t ev_start, hipEvent_t ev_stop, int launches,
+                             unsigned long long wait_ticks) {
     if (B > kMaxFusedB) return hipErrorNotSupported;
     char *wsb = static_cast<char *>(ws);
     uint64_t *keys = reinterpret_cast<uint64_t *>(wsb + ws_keys_offset());
@@ -1119,15 +813,15 @@ hipError_t launch_fused_step(const uint16_t *hidden, const uint16_t *w, float bi
     // the root workgroups, and plain stream workgroups up to the stream's
     // target, when the whole grid is resident at once and its waves fit the
     // key layout
-    const int forced = forced_launches();
-    if ((mode == DSPARK_CUT_THRESHOLD || mode == DSPARK_CUT_STATIC) && forced != 2 &&
-        (B >= kOneLaunchMinB || forced == 1)) {
+    if ((mode == DSPARK_CUT_THRESHOLD || mode == DSPARK_CUT_STATIC) && launches != 2 &&
+        (B >= kOneLaunchMinB || launches == 1)) {
         OneParams q;
         q.f = fp;
         q.s = p;
         q.gemv_done = arrivals;
-        q.go = reinterpret_cast<unsigned *>(wsb + ws_ctrl_offset() + kCtrlGoOffset);
+        q.go = reinterpret_cast<int *>(wsb + ws_ctrl_offset() + kCtrlGoOffset);
         q.timed_out = reinterpret_cast<unsigned *>(wsb + ws_ctrl_offset() + kCtrlTimedOutOffset);
+        q.wait_ticks = wait_ticks ? wait_ticks : kWaitTicks;
         q.gemv_wgs = B < cus ? B : cus;
         q.root_wgs = (int)root_wgs;
         q.lead = (int64_t)(kLead * (double)((int64_t)B * Vv / root_waves));
@@ -1143,40 +837,6 @@ hipError_t launch_fused_step(const uint16_t *hidden, const uint16_t *w, float bi
             else
                 e = vvec ? launch_one_v<false, true>(q, grid, lds, s, ev_start, ev_stop, &done)
                          : launch_one_v<false, false>(q, grid, lds, s, ev_start, ev_stop, &done);
-            if (e != hipSuccess || done) return e;
-        }
-    }
-
-    // one launch for batch-wide picks (budget and combined cuts), on request
-    // only: the head by one wave per hidden row, the pick in workgroup 0 while
-    // the others stream the root rows, then the draft rows. Measured slower
-    // than two launches at B = 256 (mixed workload budget arm 76 us against
-    // 69 us; d = 7168, T = 768: 72 against 68-70 us): the pick lands after the
-    // root rows, and the draft phase keeps the same tail. The same grid as the
-    // front of two launches (head, pick and root rows only, then the stream
-    // kernel) measured no faster than the request-workgroup front either
-    // (72.8 against 69.5 us).
-    if ((mode == DSPARK_CUT_BUDGET || mode == DSPARK_CUT_COMBINED) && forced == 1 &&
-        N <= kPickSlots && N <= kFusedSelMax && (!hvec || d <= kFrontMaxLdsW)) {
-        PickParams q;
-        q.f = fp;
-        q.s = p;
-        q.slots = reinterpret_cast<uint64_t *>(wsb + ws_pslot_offset());
-        q.go = reinterpret_cast<unsigned *>(wsb + ws_ctrl_offset() + kCtrlGoOffset);
-        q.timed_out = reinterpret_cast<unsigned *>(wsb + ws_ctrl_offset() + kCtrlTimedOutOffset);
-        size_t head = (size_t)N * 8;
-        if (hvec && (size_t)d * 2 > head) head = (size_t)d * 2;
-        const size_t lds = ((head + 15) & ~(size_t)15) + (size_t)(2 * B + 1) * 4;
-        const int want = (int)(p.target_waves / (kFrontThreads / kWave));
-        if ((int64_t)want * (kFrontThreads / kWave) <= kMaxWaves) {
-            bool done = false;
-            hipError_t e;
-            if (hvec)
-                e = vvec ? launch_pick_v<true, true>(q, want, lds, s, ev_start, ev_stop, &done)
-                         : launch_pick_v<true, false>(q, want, lds, s, ev_start, ev_stop, &done);
-            else
-                e = vvec ? launch_pick_v<false, true>(q, want, lds, s, ev_start, ev_stop, &done)
-                         : launch_pick_v<false, false>(q, want, lds, s, ev_start, ev_stop, &done);
             if (e != hipSuccess || done) return e;
         }
     }

@@ -264,27 +264,23 @@ dspark_status dspark_cap_accept(const int32_t *packed_argmax_full, const int32_t
  * conf and survival may be NULL when the caller does not want them. ws must be
  * zero-filled before its first use with this entry point (dspark_workspace_init
  * does it on a stream): its first 256 bytes hold control words, followed by
- * 32 KiB of per-request counters of this entry point, 32 KiB of those of
- * dspark_accept and 32 KiB of score slots, all of which every call returns to
- * zero on completion, at the same offsets for every size, so one workspace
- * serves calls of any sizes it is large enough for. The rest is scratch. Calls that share a
- * workspace must not overlap in time. Batches above 4096 requests run the same
- * step through the stage kernels.
+ * 32 KiB of per-request counters of this entry point and 32 KiB of those of
+ * dspark_accept, at the same offsets for every size, so one workspace serves
+ * calls of any sizes it is large enough for. The rest is scratch. Calls that
+ * share a workspace must not overlap in time. Batches above 4096 requests run
+ * the same step through the stage kernels.
  *
  * Threshold and static cuts from 96 requests up run in one launch whose
  * workgroups wait once, for the verify lengths that its first workgroups
  * compute; the grid is sized to be resident on the device at once (otherwise,
  * and for smaller batches and budget or combined cuts, the step takes two
- * launches). Budget and combined cuts have a one-launch form too (B*gamma up
- * to 4096), taken only on request: one workgroup waits for every position's
- * score and picks while the others stream the root rows, then all wait once
- * for the lengths. Those waits are bounded (about one second): a workgroup
- * that gives up sets the 32-bit word at byte 192 of ws to 1 and leaves; the
- * outputs of that call are then undefined and ws must be initialised again.
- * It does not happen while the device runs nothing else that holds its
- * compute units for that long. DSPARK_STEP_LAUNCHES=1 or 2 in the
- * environment selects the one- or two-launch form where both apply (same
- * results, bit for bit).
+ * launches). The wait is bounded (about one second): a workgroup that gives up
+ * leaves without streaming its share, and the 32-bit word at byte 192 of ws
+ * becomes 1 and stays 1 until dspark_step_status reads it. The outputs of the
+ * call that gave up are undefined; later calls on the same workspace are not
+ * affected (every call starts its counters afresh), so no re-initialisation is
+ * needed. A give-up does not happen while the device runs nothing else that
+ * holds its compute units for that long.
  */
 dspark_status dspark_step(const dspark_bf16 *hidden, const dspark_bf16 *w, float bias,
                           const float *temps, const int32_t *tokens, const dspark_bf16 *logits,
@@ -295,23 +291,41 @@ dspark_status dspark_step(const dspark_bf16 *hidden, const dspark_bf16 *w, float
                           void *ws, size_t ws_bytes, void *stream);
 
 /*
- * Measurement aid: dspark_step, plus hipEventRecord(ev_start, stream) right
- * before the launch of the step's dominant kernel (in one launch, the whole
- * step; in two, the stream over the draft rows, which also writes the
- * acceptance) and hipEventRecord(ev_stop, stream) right after it, so the
- * elapsed time between the two events is that kernel's duration. ev_start / ev_stop are hipEvent_t handles (as void*) the caller
- * created with timing enabled; either may be NULL. Results are identical to
- * dspark_step's; nothing is allocated.
+ * dspark_step with explicit controls, for measurement and testing. Results are
+ * identical to dspark_step's for every value of the controls (bit for bit, and
+ * whichever form runs); nothing is allocated.
+ *   ev_start, ev_stop: hipEvent_t handles (as void*, created by the caller with
+ *     timing enabled; either may be NULL), recorded on `stream` right before
+ *     and right after the launch of the step's dominant kernel (in one launch,
+ *     the whole step; in two, the stream over the draft rows, which also
+ *     writes the acceptance), so the time between them is that kernel's.
+ *   launches: 0 lets the library choose the form by size (as dspark_step
+ *     does), 1 asks for the one-launch form where the cut allows it (threshold
+ *     and static cuts, grid resident at once), 2 for two launches;
+ *     DSPARK_ERR_ARG for any other value.
+ *   wait_ticks: bound of the one-launch form's wait for the lengths, in ticks
+ *     of the device's 100 MHz constant clock; 0 means the default (about one
+ *     second). A bound too short for the lengths makes workgroups give up, as
+ *     described under dspark_step; tests use it to drive that path.
  */
-dspark_status dspark_step_profiled(const dspark_bf16 *hidden, const dspark_bf16 *w, float bias,
-                                   const float *temps, const int32_t *tokens,
-                                   const dspark_bf16 *logits, int B, int gamma, int d, int V,
-                                   int mode, const float *cutoff, long long budget, float *conf,
-                                   float *survival, int32_t *lengths, int32_t *cu_seqlens,
-                                   int32_t *packed_tokens, int32_t *packed_src_row,
-                                   int32_t *packed_argmax, int32_t *accepted, int32_t *bonus,
-                                   void *ws, size_t ws_bytes, void *stream, void *ev_start,
-                                   void *ev_stop);
+dspark_status dspark_step_ex(const dspark_bf16 *hidden, const dspark_bf16 *w, float bias,
+                             const float *temps, const int32_t *tokens, const dspark_bf16 *logits,
+                             int B, int gamma, int d, int V, int mode, const float *cutoff,
+                             long long budget, float *conf, float *survival, int32_t *lengths,
+                             int32_t *cu_seqlens, int32_t *packed_tokens,
+                             int32_t *packed_src_row, int32_t *packed_argmax, int32_t *accepted,
+                             int32_t *bonus, void *ws, size_t ws_bytes, void *stream,
+                             void *ev_start, void *ev_stop, int launches,
+                             unsigned long long wait_ticks);
+
+/*
+ * The fused step's give-up flag: enqueues on `stream` a read of the 32-bit word
+ * at byte 192 of ws into status[0] (device int32: 0 when no workgroup of any
+ * dspark_step / dspark_step_ex call since the last read gave up its bounded
+ * wait, 1 otherwise) and clears the word, without synchronising. ws: the
+ * workspace those calls used (16-byte aligned).
+ */
+dspark_status dspark_step_status(void *ws, int32_t *status, void *stream);
 
 /* Scratch bytes needed by dspark_accept and dspark_step for these sizes
  * (independent of d); 0 for invalid sizes. */

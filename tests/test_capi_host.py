@@ -162,8 +162,9 @@ def test_step_validation(L):
     assert step_call(L, wsb=100) == EWS
 
 
-def test_step_profiled_validation(L):
-    # the same checks as dspark_step (events are optional handles)
+def test_step_ex_validation(L):
+    # the same checks as dspark_step (events are optional handles), and the form
+    # must be 0, 1 or 2
     base = dict(hidden=A, w=A, bias=0.0, temps=A, tokens=A, logits=A, B=4, g=8, d=256, V=1024,
                 mode=0, cutoff=A, budget=0, conf=A, surv=A, lengths=A, cu=A, ptok=A, psrc=A,
                 pam=A, acc=A, bonus=A, ws=A, wsb=1 << 30)
@@ -172,17 +173,27 @@ def test_step_profiled_validation(L):
     def call(**kw):
         a = dict(base)
         a.update(kw)
-        return L.dspark_step_profiled(
+        return L.dspark_step_ex(
             f(a["hidden"]), f(a["w"]), a["bias"], f(a["temps"]), f(a["tokens"]), f(a["logits"]),
             a["B"], a["g"], a["d"], a["V"], a["mode"], f(a["cutoff"]), a["budget"], f(a["conf"]),
             f(a["surv"]), f(a["lengths"]), f(a["cu"]), f(a["ptok"]), f(a["psrc"]), f(a["pam"]),
-            f(a["acc"]), f(a["bonus"]), f(a["ws"]), a["wsb"], None, None, None)
+            f(a["acc"]), f(a["bonus"]), f(a["ws"]), a["wsb"], None, None, None,
+            a.get("launches", 0), a.get("ticks", 0))
 
     assert call(logits=0) == ENULL
+    assert call(launches=3) == EARG
+    assert call(launches=-1) == EARG
     assert call(B=0) == ESHAPE
     assert call(mode=9) == EARG
     assert call(ws=A + 4) == EALIGN
     assert call(wsb=100) == EWS
+
+
+def test_step_status_validation(L):
+    assert L.dspark_step_status(None, P(A), None) == ENULL
+    assert L.dspark_step_status(P(A), None, None) == ENULL
+    assert L.dspark_step_status(P(A + 4), P(A), None) == EALIGN
+    assert L.dspark_step_status(P(A), P(A + 2), None) == EALIGN
 
 
 def cap_call(L, pam=A, tok=A, lengths=A, B=4, g=8, acc=A, bon=A, full=A, sums=0):

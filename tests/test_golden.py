@@ -131,13 +131,11 @@ def _gpu_step(doc, inputs, case, launches, monkeypatch):
             torch.bfloat16).to(dev)
 
     c = _cutoff(doc, case)
-    monkeypatch.setenv("DSPARK_STEP_LAUNCHES", str(launches))
     out = dspark.dspark_step(bf(hidden), bf(wb), doc["bias"], torch.from_numpy(temps).to(dev),
                              torch.from_numpy(tokens).to(dev), bf(logits), case["mode"],
                              cutoff=None if c is None else torch.from_numpy(c).to(dev),
-                             budget=case["budget"])
+                             budget=case["budget"], launches=launches)
     torch.cuda.synchronize()
-    monkeypatch.delenv("DSPARK_STEP_LAUNCHES", raising=False)
     return {k: v.cpu().numpy() for k, v in out.items()}
 
 

@@ -42,21 +42,19 @@ def _cases():
     return out
 
 
-def _run(s, form, monkeypatch):
-    monkeypatch.setenv("DSPARK_STEP_LAUNCHES", form)
+def _run(s, launches):
     out = dspark.dspark_step(s.hidden, s.w, s.bias, s.temps, s.tokens, s.logits, s.cfg.mode,
-                             cutoff=s.cutoff, budget=s.budget)
+                             cutoff=s.cutoff, budget=s.budget, launches=launches)
     torch.cuda.synchronize()
-    monkeypatch.delenv("DSPARK_STEP_LAUNCHES", raising=False)
     return {k: v.cpu().numpy() for k, v in out.items()}
 
 
-def test_random_shapes_both_forms_match_the_oracle(monkeypatch):
+def test_random_shapes_both_forms_match_the_oracle():
     amb = 0
     for c, cfg in enumerate(_cases()):
         s = make_step(cfg, c, device=DEV)
-        one = _run(s, "1", monkeypatch)
-        two = _run(s, "2", monkeypatch)
+        one = _run(s, 1)
+        two = _run(s, 2)
         tag = f"case {c}: B={cfg.B} gamma={cfg.gamma} d={cfg.d} V={cfg.V} {cfg.mode} T={s.budget}"
         for k in one:
             assert np.array_equal(one[k], two[k]), f"{tag}: {k} differs between forms"

@@ -1,13 +1,14 @@
 """The fused step's two forms (needs an MI355X).
 
-Every cut runs the whole step in one launch from 96 requests up, in two
-below; the environment variable DSPARK_STEP_LAUNCHES (1 or 2) selects a form
-for any size. Threshold and static cuts take step_one_kernel as their one
-launch; budget and combined cuts take step_pick_kernel (the head one hidden
-row per wave, the batch-wide pick in workgroup 0) while B*gamma <= 4096 and
-two launches beyond. Both forms must match the oracle, match each other bit
-for bit, and leave the workspace's counters and score slots at zero, so that
-calls of either form can follow each other on one workspace.
+Threshold and static cuts run the whole step in one launch from 96 requests up
+and in two below; budget and combined cuts run in two. dspark_step_ex's
+`launches` argument (1 or 2) selects a form for any size where the cut allows
+it. Both forms must match the oracle, match each other bit for bit, and leave
+the workspace's counters at zero, so that calls of either form can follow each
+other on one workspace. The one-launch form's bounded wait is driven to give
+up from the host (a wait bound of one clock tick): the give-up must be reported
+by dspark_step_status, every kernel must still finish, and the next call on
+the same workspace must be exact without re-initialising it.
 """
 import numpy as np
 import pytest
@@ -23,20 +24,24 @@ pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
 CTRL_BYTES = 256       # control words at the start of the workspace
 MAX_FUSED_B = 4096     # per-request counters that follow them (uint64 each)
-PICK_SLOTS = 4096      # score slots of the one-launch pick, after both counter sets
 
 
 def _host(out):
     return {k: v.cpu().numpy() for k, v in out.items()}
 
 
-def _step(s, ws, two_launches, monkeypatch):
-    monkeypatch.setenv("DSPARK_STEP_LAUNCHES", "2" if two_launches else "1")
+def _step(s, ws, two_launches, wait_ticks=0):
     out = dspark.dspark_step(s.hidden, s.w, s.bias, s.temps, s.tokens, s.logits, s.cfg.mode,
-                             cutoff=s.cutoff, budget=s.budget, ws=ws)
+                             cutoff=s.cutoff, budget=s.budget, ws=ws,
+                             launches=2 if two_launches else 1, wait_ticks=wait_ticks)
     torch.cuda.synchronize()
-    monkeypatch.delenv("DSPARK_STEP_LAUNCHES", raising=False)
     return _host(out)
+
+
+def _status(ws):
+    st = dspark.dspark_step_status(ws)
+    torch.cuda.synchronize()
+    return int(st.item())
 
 
 def _fresh_ws(cfg):
@@ -49,9 +54,7 @@ def _fresh_ws(cfg):
 
 def _counters_zero(ws, B):
     head = ws[: CTRL_BYTES + 8 * min(B, MAX_FUSED_B)].cpu().numpy()
-    slot0 = CTRL_BYTES + 16 * MAX_FUSED_B
-    slots = ws[slot0: slot0 + 8 * PICK_SLOTS].cpu().numpy()
-    return int(np.count_nonzero(head)) == 0 and int(np.count_nonzero(slots)) == 0
+    return int(np.count_nonzero(head)) == 0
 
 
 CASES = {
@@ -64,9 +67,10 @@ CASES = {
     # the largest batch of the fused step: each request workgroup runs 16
     # requests, and cu_seqlens fills 32 KiB of LDS
     "max_batch": CONFIGS["tiny"].scaled(B=4096, gamma=4, d=128, V=512),
-    # batch-wide picks: B*gamma = 4096 positions, the most the one-launch pick
-    # takes; d = 7168 stages a 14 KiB head; odd d and V take the scalar paths;
-    # a batch over 4096 positions takes two launches under either setting
+    # batch-wide picks (two launches under either setting): B*gamma = 4096
+    # positions, the most the in-kernel pick takes; d = 7168 stages a 14 KiB
+    # head; odd d and V take the scalar paths; a batch over 4096 positions
+    # takes the stage kernel's pick
     "mixed_budget": CONFIGS["mixed_budget"].scaled(V=32768),
     "budget_d7168": CONFIGS["budget"].scaled(V=16384),
     "mixed_combined": CONFIGS["mixed_combined"].scaled(V=32768),
@@ -88,16 +92,16 @@ TIED = ("tied_budget", "tied_combined")
 
 
 @pytest.mark.parametrize("name", list(CASES))
-def test_both_forms_match_the_oracle_and_each_other(name, monkeypatch):
+def test_both_forms_match_the_oracle_and_each_other(name):
     cfg = CASES[name]
     ws = _fresh_ws(cfg)
     for step in range(2):
         s = make_step(cfg, step, device=DEV)
         if name in TIED:
             s.hidden.zero_()
-        one = _step(s, ws, False, monkeypatch)
+        one = _step(s, ws, False)
         assert _counters_zero(ws, cfg.B), f"{name}: counters left set by the one-launch form"
-        two = _step(s, ws, True, monkeypatch)
+        two = _step(s, ws, True)
         assert _counters_zero(ws, cfg.B), f"{name}: counters left set by the two-launch form"
         for k in one:
             assert np.array_equal(one[k], two[k]), f"{name} step {step}: {k} differs between forms"
@@ -112,19 +116,52 @@ def test_both_forms_match_the_oracle_and_each_other(name, monkeypatch):
         front = oracle_front(h)
         compare(one, oracle_back(h, front, *oracle_rows(s, front)), h.tokens,
                 ctx=f"{name} step {step}")
+    assert _status(ws) == 0, f"{name}: a wait gave up"
 
 
-def test_forms_alternate_on_one_workspace(monkeypatch):
+def test_forms_alternate_on_one_workspace():
     # one form after the other, repeatedly, on the same workspace: each call
     # must start from the counters the previous one returned to zero
     cfg = CONFIGS["mixed_threshold"].scaled(B=64, V=16384)
     ws = _fresh_ws(cfg)
     steps = [make_step(cfg, i, device=DEV) for i in range(3)]
     steps.append(make_step(CONFIGS["mixed_budget"].scaled(B=64, V=16384), 0, device=DEV))
-    ref = [_step(s, ws, False, monkeypatch) for s in steps]
+    ref = [_step(s, ws, False) for s in steps]
     for rnd in range(4):
         for i, s in enumerate(steps):
-            got = _step(s, ws, (rnd + i) % 2 == 1, monkeypatch)
+            got = _step(s, ws, (rnd + i) % 2 == 1)
             for k in got:
                 assert np.array_equal(got[k], ref[i][k]), f"round {rnd} step {i}: {k}"
     assert _counters_zero(ws, cfg.B)
+
+
+def test_give_up_is_reported_and_the_next_call_is_exact():
+    # B = 128 takes the one-launch form; its grid holds idle stream workgroups
+    # that wait for the lengths from their first instruction, so a bound of one
+    # tick of the 100 MHz clock makes them give up. Every kernel still ends:
+    # the give-up path only sets the flag, leaves the go word and returns.
+    cfg = CONFIGS["mixed_threshold"].scaled(B=128, V=16384)
+    ws = _fresh_ws(cfg)
+    steps = [make_step(cfg, i, device=DEV) for i in range(2)]
+    ref = [_step(s, ws, False) for s in steps]
+    assert _status(ws) == 0
+    _step(steps[0], ws, False, wait_ticks=1)
+    assert _status(ws) == 1, "the give-up was not reported"
+    assert _status(ws) == 0, "the status read must clear the flag"
+    # the next calls on the same workspace, not re-initialised, are exact
+    for i, s in enumerate(steps):
+        got = _step(s, ws, False)
+        for k in got:
+            assert np.array_equal(got[k], ref[i][k]), f"after the give-up, step {i}: {k}"
+        h = snapshot(s)
+        front = oracle_front(h)
+        compare(got, oracle_back(h, front, *oracle_rows(s, front)), h.tokens,
+                ctx=f"after the give-up, step {i}")
+    assert _status(ws) == 0
+    assert _counters_zero(ws, cfg.B)
+    # and so is the two-launch form after another give-up
+    _step(steps[1], ws, False, wait_ticks=1)
+    got = _step(steps[1], ws, True)
+    assert _status(ws) == 1
+    for k in got:
+        assert np.array_equal(got[k], ref[1][k]), f"two launches after a give-up: {k}"

@@ -114,7 +114,7 @@ def test_step_graph_replays_match_eager(name, B):
 
 @pytest.mark.parametrize("name", ["mixed_threshold", "mixed_budget"])
 def test_profiled_step_matches_step_and_brackets_the_dominant_kernel(name):
-    # dspark_step_profiled gives dspark_step's results and records its events
+    # dspark_step_ex with timing events gives dspark_step's results and records them
     # around the dominant kernel, inside the step's own event pair: the whole
     # step in one launch (per-request cutoff, B = 128), the stream kernel of
     # two launches (budget)
@@ -125,8 +125,8 @@ def test_profiled_step_matches_step_and_brackets_the_dominant_kernel(name):
     ref = {k: v.cpu().numpy() for k, v in ref.items()}
     e = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
     e[0].record()
-    got = dspark.dspark_step_profiled(s.hidden, s.w, s.bias, s.temps, s.tokens, s.logits,
-                                      cfg.mode, (e[1], e[2]), cutoff=s.cutoff, budget=s.budget)
+    got = dspark.dspark_step_ex(s.hidden, s.w, s.bias, s.temps, s.tokens, s.logits, cfg.mode,
+                                cutoff=s.cutoff, budget=s.budget, events=(e[1], e[2]))
     e[3].record()
     torch.cuda.synchronize()
     for k, v in got.items():
