@@ -59,6 +59,7 @@ def lib() -> ctypes.CDLL:
         L.dspark_cost_cutoff.argtypes = [P, I, P, I, P, P]
         L.dspark_step_ex.argtypes = L.dspark_step.argtypes + [P, P, I, ctypes.c_ulonglong]
         L.dspark_step_status.argtypes = [P, P, P]
+        L.dspark_step_noalloc.argtypes = L.dspark_step.argtypes[:22] + [P, P]
         L.dspark_workspace_bytes.argtypes = [I, I, I]
         L.dspark_workspace_bytes.restype = S
         L.dspark_workspace_init.argtypes = [P, S, P]
@@ -67,7 +68,7 @@ def lib() -> ctypes.CDLL:
         for f in (L.dspark_confidence, L.dspark_schedule, L.dspark_compact, L.dspark_accept,
                   L.dspark_step, L.dspark_workspace_init, L.dspark_cap_accept,
                   L.dspark_gather_rows, L.dspark_tier_select, L.dspark_cost_cutoff,
-                  L.dspark_step_ex, L.dspark_step_status):
+                  L.dspark_step_ex, L.dspark_step_status, L.dspark_step_noalloc):
             f.restype = ctypes.c_int
         _lib = L
     return _lib
@@ -430,6 +431,36 @@ def dspark_step_ex(hidden, w, bias, temps, tokens, logits, mode, cutoff=None, bu
                        wait_ticks=wait_ticks)
 
 
+def dspark_step_noalloc(hidden, w, bias, temps, tokens, logits, mode, cutoff=None, budget=0,
+                        out=None, status=None):
+    """dspark_step without a workspace argument: the library's own per-device
+    scratch array serves as the workspace, so the call allocates nothing on the
+    device side (torch allocates the outputs here only when `out` is None).
+    `status` (int32 [1], optional) receives the give-up flag of this call.
+    Calls on one device share that scratch and must not overlap in time."""
+    B, g, d = hidden.shape
+    V = logits.shape[-1]
+    _need(hidden, "hidden", torch.bfloat16)
+    _need(w, "w", torch.bfloat16, (d,))
+    _need(temps, "temps", torch.float32, (g,))
+    _need(tokens, "tokens", torch.int32, (B, g + 1))
+    _need(logits, "logits", torch.bfloat16, (B, g + 1, V))
+    m = _mode(mode)
+    if cutoff is not None:
+        _need(cutoff, "cutoff", torch.float32, (B,))
+    dev = hidden.device
+    out = alloc_step_outputs(B, g, dev) if out is None else out
+    if status is not None:
+        _need(status, "status", torch.int32, (1,))
+    _ok("dspark_step_noalloc", lib().dspark_step_noalloc(
+        _ptr(hidden), _ptr(w), float(bias), _ptr(temps), _ptr(tokens), _ptr(logits), B, g, d, V,
+        m, _ptr(cutoff), int(budget), _ptr(out.get("conf")), _ptr(out.get("survival")),
+        _ptr(out["lengths"]), _ptr(out["cu_seqlens"]), _ptr(out["packed_tokens"]),
+        _ptr(out["packed_src_row"]), _ptr(out["packed_argmax"]), _ptr(out["accepted"]),
+        _ptr(out["bonus"]), _ptr(status), _stream(dev)))
+    return out
+
+
 def dspark_step_status(ws=None, status=None, device=None):
     """The fused step's give-up flag of a workspace, read and cleared on the
     device: an int32 [1] tensor, 0 when no call since the last read gave up its
@@ -448,7 +479,7 @@ def dspark_step_status(ws=None, status=None, device=None):
 __all__ = ["DsparkError", "lib", "LIB_PATH", "dspark_status_string", "dspark_confidence", "dspark_schedule",
            "dspark_compact", "dspark_accept", "dspark_step", "dspark_cap_accept",
            "dspark_gather_rows", "dspark_tier_select", "dspark_cost_cutoff",
-           "dspark_step_ex", "dspark_step_status",
+           "dspark_step_ex", "dspark_step_status", "dspark_step_noalloc",
            "dspark_workspace_bytes",
            "dspark_workspace_init", "workspace", "alloc_step_outputs", "STEP_OUTPUTS",
            "DSPARK_CUT_THRESHOLD", "DSPARK_CUT_BUDGET", "DSPARK_CUT_STATIC",

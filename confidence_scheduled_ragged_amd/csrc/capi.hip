@@ -2,6 +2,7 @@
 // the caller's stream. No allocation, no synchronisation, no per-call state.
 #include <atomic>
 #include <cmath>
+#include <mutex>
 
 #include "common.hpp"
 
@@ -236,17 +237,17 @@ DSPARK_API dspark_status dspark_cap_accept(const int32_t *packed_argmax_full,
                                       bonus, accepted_full, sums, as_stream(stream)));
 }
 
-static dspark_status step_impl(const dspark_bf16 *hidden, const dspark_bf16 *w, float bias,
-                               const float *temps, const int32_t *tokens,
-                               const dspark_bf16 *logits, int B, int gamma, int d, int V,
-                               int mode, const float *cutoff, long long budget, float *conf,
-                               float *survival, int32_t *lengths, int32_t *cu_seqlens,
-                               int32_t *packed_tokens, int32_t *packed_src_row,
-                               int32_t *packed_argmax, int32_t *accepted, int32_t *bonus,
-                               void *ws, size_t ws_bytes, void *stream, void *ev_start,
-                               void *ev_stop, int launches, unsigned long long wait_ticks) {
+// Host-side checks of the fused step's arguments (every one but the workspace).
+static dspark_status step_check(const dspark_bf16 *hidden, const dspark_bf16 *w, float bias,
+                                const float *temps, const int32_t *tokens,
+                                const dspark_bf16 *logits, int B, int gamma, int d, int V,
+                                int mode, const float *cutoff, long long budget, float *conf,
+                                float *survival, int32_t *lengths, int32_t *cu_seqlens,
+                                int32_t *packed_tokens, int32_t *packed_src_row,
+                                int32_t *packed_argmax, int32_t *accepted, int32_t *bonus,
+                                int launches) {
     if (!hidden || !w || !temps || !tokens || !logits || !lengths || !cu_seqlens ||
-        !packed_tokens || !packed_src_row || !packed_argmax || !accepted || !bonus || !ws)
+        !packed_tokens || !packed_src_row || !packed_argmax || !accepted || !bonus)
         return DSPARK_ERR_NULL;
     if (needs_cutoff(mode) && !cutoff) return DSPARK_ERR_NULL;
     if (dspark_status st = check_bg(B, gamma)) return st;
@@ -260,10 +261,21 @@ static dspark_status step_impl(const dspark_bf16 *hidden, const dspark_bf16 *w, 
         misaligned(conf, 4) || misaligned(survival, 4) || misaligned(lengths, 4) ||
         misaligned(cu_seqlens, 4) || misaligned(packed_tokens, 4) ||
         misaligned(packed_src_row, 4) || misaligned(packed_argmax, 4) ||
-        misaligned(accepted, 4) || misaligned(bonus, 4) || misaligned(ws, 16))
+        misaligned(accepted, 4) || misaligned(bonus, 4))
         return DSPARK_ERR_ALIGN;
-    if (ws_bytes < ws_total_bytes(B, gamma)) return DSPARK_ERR_WORKSPACE;
-    hipStream_t s = as_stream(stream);
+    return DSPARK_OK;
+}
+
+// The fused step's launches, after every check has passed.
+static dspark_status step_launch(const dspark_bf16 *hidden, const dspark_bf16 *w, float bias,
+                                 const float *temps, const int32_t *tokens,
+                                 const dspark_bf16 *logits, int B, int gamma, int d, int V,
+                                 int mode, const float *cutoff, long long budget, float *conf,
+                                 float *survival, int32_t *lengths, int32_t *cu_seqlens,
+                                 int32_t *packed_tokens, int32_t *packed_src_row,
+                                 int32_t *packed_argmax, int32_t *accepted, int32_t *bonus,
+                                 void *ws, hipStream_t s, void *ev_start, void *ev_stop,
+                                 int launches, unsigned long long wait_ticks) {
     char *wsb = static_cast<char *>(ws);
     float *surv = survival ? survival : reinterpret_cast<float *>(wsb + ws_surv_offset(B, gamma));
     float *cf = conf ? conf : reinterpret_cast<float *>(wsb + ws_conf_offset(B, gamma));
@@ -284,6 +296,29 @@ static dspark_status step_impl(const dspark_bf16 *hidden, const dspark_bf16 *w, 
                           accepted, bonus, ws, s);
     if (e == hipSuccess && et) e = hipEventRecord(et, s);
     return launched(e);
+}
+
+static dspark_status step_impl(const dspark_bf16 *hidden, const dspark_bf16 *w, float bias,
+                               const float *temps, const int32_t *tokens,
+                               const dspark_bf16 *logits, int B, int gamma, int d, int V,
+                               int mode, const float *cutoff, long long budget, float *conf,
+                               float *survival, int32_t *lengths, int32_t *cu_seqlens,
+                               int32_t *packed_tokens, int32_t *packed_src_row,
+                               int32_t *packed_argmax, int32_t *accepted, int32_t *bonus,
+                               void *ws, size_t ws_bytes, void *stream, void *ev_start,
+                               void *ev_stop, int launches, unsigned long long wait_ticks) {
+    if (dspark_status st = step_check(hidden, w, bias, temps, tokens, logits, B, gamma, d, V, mode,
+                                      cutoff, budget, conf, survival, lengths, cu_seqlens,
+                                      packed_tokens, packed_src_row, packed_argmax, accepted,
+                                      bonus, launches))
+        return st;
+    if (!ws) return DSPARK_ERR_NULL;
+    if (misaligned(ws, 16)) return DSPARK_ERR_ALIGN;
+    if (ws_bytes < ws_total_bytes(B, gamma)) return DSPARK_ERR_WORKSPACE;
+    return step_launch(hidden, w, bias, temps, tokens, logits, B, gamma, d, V, mode, cutoff,
+                       budget, conf, survival, lengths, cu_seqlens, packed_tokens, packed_src_row,
+                       packed_argmax, accepted, bonus, ws, as_stream(stream), ev_start, ev_stop,
+                       launches, wait_ticks);
 }
 
 DSPARK_API dspark_status dspark_step(const dspark_bf16 *hidden, const dspark_bf16 *w, float bias,
@@ -316,4 +351,61 @@ DSPARK_API dspark_status dspark_step_status(void *ws, int32_t *status, void *str
     if (!ws || !status) return DSPARK_ERR_NULL;
     if (misaligned(ws, 16) || misaligned(status, 4)) return DSPARK_ERR_ALIGN;
     return launched(launch_step_status(ws, status, as_stream(stream)));
+}
+
+// ------------------------------------------------------------ no allocation
+
+// The workspace of dspark_step_noalloc: one array per device, in the code
+// object's own device memory, so the call allocates nothing. In host code the
+// name `scratch` is only a stand-in for the symbol; its device address (one per
+// device) comes from hipGetSymbolAddress and is the only pointer ever passed to
+// a kernel or a fill.
+constexpr size_t kNoallocScratchBytes = (size_t)4 << 20;
+static __device__ __align__(256) unsigned char scratch[kNoallocScratchBytes];
+
+namespace {
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[64];  // device address of `scratch` per device, once set up
+}  // namespace
+
+// The current device's scratch address. The first call on a device looks it up
+// and zero-fills the array on `s` (the fused step's control words and counters
+// must start at zero; every call returns them to zero).
+static dspark_status noalloc_scratch(void **out, hipStream_t s) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return DSPARK_ERR_HIP;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void *p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p)
+            return DSPARK_ERR_HIP;
+        if (launch_fill_zero(p, kNoallocScratchBytes, s) != hipSuccess) return DSPARK_ERR_HIP;
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return DSPARK_OK;
+}
+
+DSPARK_API dspark_status dspark_step_noalloc(
+    const dspark_bf16 *hidden, const dspark_bf16 *w, float bias, const float *temps,
+    const int32_t *tokens, const dspark_bf16 *logits, int B, int gamma, int d, int V, int mode,
+    const float *cutoff, long long budget, float *conf, float *survival, int32_t *lengths,
+    int32_t *cu_seqlens, int32_t *packed_tokens, int32_t *packed_src_row, int32_t *packed_argmax,
+    int32_t *accepted, int32_t *bonus, int32_t *status, void *stream) {
+    if (dspark_status st = step_check(hidden, w, bias, temps, tokens, logits, B, gamma, d, V, mode,
+                                      cutoff, budget, conf, survival, lengths, cu_seqlens,
+                                      packed_tokens, packed_src_row, packed_argmax, accepted,
+                                      bonus, 0))
+        return st;
+    if (ws_total_bytes(B, gamma) > kNoallocScratchBytes) return DSPARK_ERR_WORKSPACE;
+    if (misaligned(status, 4)) return DSPARK_ERR_ALIGN;
+    hipStream_t s = as_stream(stream);
+    void *ws = nullptr;
+    if (dspark_status st = noalloc_scratch(&ws, s)) return st;
+    dspark_status st = step_launch(hidden, w, bias, temps, tokens, logits, B, gamma, d, V, mode,
+                                   cutoff, budget, conf, survival, lengths, cu_seqlens,
+                                   packed_tokens, packed_src_row, packed_argmax, accepted, bonus,
+                                   ws, s, nullptr, nullptr, 0, 0);
+    if (st == DSPARK_OK && status) st = launched(launch_step_status(ws, status, s));
+    return st;
 }

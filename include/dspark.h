@@ -327,6 +327,32 @@ dspark_status dspark_step_ex(const dspark_bf16 *hidden, const dspark_bf16 *w, fl
  */
 dspark_status dspark_step_status(void *ws, int32_t *status, void *stream);
 
+/*
+ * dspark_step for callers that cannot allocate device memory at all: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc, where even a caller-owned workspace is unavailable. The
+ * arguments and results are dspark_step's, without ws and ws_bytes: the
+ * library's own scratch array in device memory (4 MiB per device, held until
+ * the process ends) serves as the workspace. The first call on a device looks
+ * the array up and zero-fills it on `stream`; later calls find its counters
+ * back at zero. Nothing is allocated or freed by any call.
+ *   status (nullable) [1] int32 device output: the call's give-up flag, read and
+ *     cleared as dspark_step_status does (0 when every bounded wait ended).
+ * DSPARK_ERR_WORKSPACE when dspark_workspace_bytes(B, gamma, V) exceeds the
+ * 4 MiB array (about 240k verify rows B*(gamma+1)); the other checks are
+ * dspark_step's. Every call on one device shares that device's array: calls
+ * that overlap in time on one device (another stream, another thread) race and
+ * give undefined results, so keep them ordered on one stream.
+ */
+dspark_status dspark_step_noalloc(const dspark_bf16 *hidden, const dspark_bf16 *w, float bias,
+                                  const float *temps, const int32_t *tokens,
+                                  const dspark_bf16 *logits, int B, int gamma, int d, int V,
+                                  int mode, const float *cutoff, long long budget, float *conf,
+                                  float *survival, int32_t *lengths, int32_t *cu_seqlens,
+                                  int32_t *packed_tokens, int32_t *packed_src_row,
+                                  int32_t *packed_argmax, int32_t *accepted, int32_t *bonus,
+                                  int32_t *status, void *stream);
+
 /* Scratch bytes needed by dspark_accept and dspark_step for these sizes
  * (independent of d); 0 for invalid sizes. */
 size_t dspark_workspace_bytes(int B, int gamma, int V);

@@ -189,6 +189,24 @@ def test_step_ex_validation(L):
     assert call(wsb=100) == EWS
 
 
+def test_step_noalloc_validation(L):
+    # the dspark_step checks, then the size of the library's scratch; every call
+    # here is rejected before the scratch (a device symbol) is looked up
+    f = lambda x: P(x) if x else None
+
+    def call(B=4, g=8, logits=A, status=0, mode=0, launches=None):
+        return L.dspark_step_noalloc(
+            f(A), f(A), 0.0, f(A), f(A), f(logits), B, g, 256, 1024, mode, f(A), 0, f(A), f(A),
+            f(A), f(A), f(A), f(A), f(A), f(A), f(A), f(status), None)
+
+    assert call(logits=0) == ENULL
+    assert call(B=0) == ESHAPE
+    assert call(mode=9) == EARG
+    assert call(B=20000, g=16) == EWS          # workspace beyond the 4 MiB scratch
+    assert call(B=200000, g=1) == EWS
+    assert call(status=A + 2) == EALIGN
+
+
 def test_step_status_validation(L):
     assert L.dspark_step_status(None, P(A), None) == ENULL
     assert L.dspark_step_status(P(A), None, None) == ENULL
