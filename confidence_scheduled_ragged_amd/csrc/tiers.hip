@@ -1,11 +1,11 @@
 // tiers.hip - graph tier of a packed verify batch, picked on the device.
 //
 // [P1] "DFlash to DSpark in SGLang", section "Ragged verify under full CUDA
-// graphs": the verify graph is keyed on the packed total rounded up to the
-// nearest captured tier; when budgets tighten the total drops to a smaller
-// tier and the replayed graph has fewer rows. The pick and the padding of the
-// packed arrays up to the tier run on the device, so they can sit in the same
-// stream (or captured graph) as the schedule and compaction.
+// graphs": graphs are captured for a ladder of packed sizes, and a step replays
+// the smallest captured size that holds its packed total, so a tighter budget
+// replays a smaller graph. The pick and the padding of the packed arrays up to
+// that size run on the device, so they can sit in the same stream (or captured
+// graph) as the schedule and compaction.
 #include "common.hpp"
 
 namespace dspark {

@@ -153,9 +153,9 @@ dspark_status dspark_compact(const int32_t *lengths, const int32_t *tokens, int 
                              dspark_bf16 *packed_logits, void *stream);
 
 /*
- * Graph tier [P1, "Ragged verify under full CUDA graphs"]: the verify graph is
- * keyed on the packed total rounded up to the nearest captured tier, and the
- * packed batch is padded to that tier.
+ * Graph tier [P1, "Ragged verify under full CUDA graphs"]: graphs are captured
+ * for a ladder of packed sizes (tiers); a step runs the smallest tier that holds
+ * its packed total, with the packed batch padded up to it.
  *   tiers [ntiers] int32 (device): the captured tier sizes, strictly
  *     ascending (not checked on the host; 1 <= ntiers <= 4096);
  *   tier_index[0]   = smallest t with tiers[t] >= cu_seqlens[B], or ntiers when

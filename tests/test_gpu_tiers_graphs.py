@@ -1,8 +1,8 @@
 """Graph tiers and HIP-graph replay of the verify step (needs an MI355X).
 
 [P1] "DFlash to DSpark in SGLang", section "Ragged verify under full CUDA
-graphs": the verify graph is keyed on the packed total rounded up to the
-nearest captured tier. dspark_tier_select picks the tier and pads the packed
+graphs": a step replays the smallest captured tier that holds its packed total.
+dspark_tier_select picks the tier and pads the packed
 arrays on the device; it is compared with the oracle's tier pick. Every launch
 shape of the library is independent of the packed total, so one captured graph
 of the whole step (plus the tier pick) replays correctly for any schedule:
