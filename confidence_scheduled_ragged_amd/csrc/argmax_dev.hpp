@@ -37,7 +37,10 @@ __device__ __forceinline__ void fold_slot(u32x4 a, int base, float &best, int &b
 
 // One lane's share of slots [v0, v1) of a row: slots v0+lane, v0+lane+64, ...
 // kVec: a slot is 8 bf16 (16-byte aligned row); otherwise a slot is one bf16.
-// kUnroll loads are issued before any is consumed.
+// kUnroll loads are issued before any is consumed. With kUnroll > 2 the last
+// partial round is one batch too: its loads past v1 are clamped to slot v1 - 1
+// (in the row, and the same cache line) and not folded, so a short segment
+// costs one memory round trip instead of one per leftover slot.
 template <bool kVec, int kUnroll>
 __device__ __forceinline__ void lane_row_segment(const uint16_t *__restrict__ row, int64_t v0,
                                                  int64_t v1, int lane, float &best, int &bidx) {
@@ -51,7 +54,22 @@ __device__ __forceinline__ void lane_row_segment(const uint16_t *__restrict__ ro
 #pragma unroll
             for (int u = 0; u < kUnroll; ++u) fold_slot(buf[u], (int)((v + u * kWave) * 8), best, bidx);
         }
-        for (; v < v1; v += kWave) fold_slot(__builtin_nontemporal_load(r4 + v), (int)(v * 8), best, bidx);
+        if (kUnroll > 2) {
+            if (v < v1) {
+                u32x4 buf[kUnroll];
+#pragma unroll
+                for (int u = 0; u < kUnroll; ++u) {
+                    const int64_t x = v + u * kWave;
+                    buf[u] = __builtin_nontemporal_load(r4 + (x < v1 ? x : v1 - 1));
+                }
+#pragma unroll
+                for (int u = 0; u < kUnroll; ++u)
+                    if (v + u * kWave < v1) fold_slot(buf[u], (int)((v + u * kWave) * 8), best, bidx);
+            }
+        } else {
+            for (; v < v1; v += kWave)
+                fold_slot(__builtin_nontemporal_load(r4 + v), (int)(v * 8), best, bidx);
+        }
     } else {
         for (int64_t v = v0 + lane; v < v1; v += kWave) {
             const float x = bf16_f32(row[v]);
@@ -135,6 +153,21 @@ __device__ __forceinline__ int32_t segment_keys_argmax(const uint64_t *__restric
     return key_index(k);
 }
 
+// The same by the calling wave: lane i reads keys s_lo + i, s_lo + i + 64, ...
+// (of row r), so up to 64 segments cost one memory round trip. Called by a
+// whole wave; every lane gets the index.
+template <bool kCoherent = false>
+__device__ __forceinline__ int32_t wave_segment_keys_argmax(const uint64_t *__restrict__ keys,
+                                                            int64_t r, int64_t s_lo, int64_t s_hi) {
+    const int lane = threadIdx.x & (kWave - 1);
+    uint64_t k = 0;
+    for (int64_t s = s_lo + lane; s <= s_hi; s += kWave) {
+        const uint64_t x = kCoherent ? load_key_coherent(keys + s + r) : keys[s + r];
+        k = x > k ? x : k;
+    }
+    return key_index(wave_max_u64(k));
+}
+
 // Argmax of packed row r from the keys of the waves whose shares (Q slots
 // each, Vv slots per row) touch it.
 template <bool kCoherent = false>
@@ -148,12 +181,12 @@ __device__ __forceinline__ int32_t row_argmax(const uint64_t *__restrict__ keys,
 // handles row j (chunks of 64 rows) and stores it at pam_b[j]. The first row j
 // where the target disagrees with draft j+1, or j = L_b, is the accepted
 // count; that row's argmax is the bonus. n <= 0 gives accepted 0, bonus -1.
-template <typename RowAm>
-__device__ __forceinline__ void wave_accept_rows(RowAm row_am, int n, int gamma,
-                                                 const int32_t *__restrict__ tok,
-                                                 int32_t *__restrict__ pam_b,
-                                                 int32_t *__restrict__ acc_b,
-                                                 int32_t *__restrict__ bonus_b) {
+// draft(j) is draft j + 1's token (asked for j < L_b only).
+template <typename RowAm, typename Draft>
+__device__ __forceinline__ void wave_accept_rows_t(RowAm row_am, Draft draft, int n, int gamma,
+                                                   int32_t *__restrict__ pam_b,
+                                                   int32_t *__restrict__ acc_b,
+                                                   int32_t *__restrict__ bonus_b) {
     const int lane = threadIdx.x & (kWave - 1);
     if (n <= 0) {
         if (lane == 0) {
@@ -172,7 +205,7 @@ __device__ __forceinline__ void wave_accept_rows(RowAm row_am, int n, int gamma,
         if (j < n) {
             am = row_am(j);
             pam_b[j] = am;
-            stop = (j >= L) || (am != tok[j + 1]);
+            stop = (j >= L) || (am != draft(j));
         }
         const uint64_t mask = __ballot(stop);
         if (a < 0 && mask != 0ull) {
@@ -185,6 +218,16 @@ __device__ __forceinline__ void wave_accept_rows(RowAm row_am, int n, int gamma,
         *acc_b = a;
         *bonus_b = bon;
     }
+}
+
+// The same with the request's tokens in memory (tok[0] the root token).
+template <typename RowAm>
+__device__ __forceinline__ void wave_accept_rows(RowAm row_am, int n, int gamma,
+                                                 const int32_t *__restrict__ tok,
+                                                 int32_t *__restrict__ pam_b,
+                                                 int32_t *__restrict__ acc_b,
+                                                 int32_t *__restrict__ bonus_b) {
+    wave_accept_rows_t(row_am, [&](int j) { return tok[j + 1]; }, n, gamma, pam_b, acc_b, bonus_b);
 }
 
 // Acceptance and bonus of request b when every packed row's argmax comes from

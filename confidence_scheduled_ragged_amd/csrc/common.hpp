@@ -36,14 +36,55 @@ __device__ __forceinline__ uint64_t argmax_key(float v, uint32_t idx) {
 __device__ __forceinline__ int32_t key_index(uint64_t k) {
     return k == 0 ? -1 : (int32_t)(0xFFFFFFFFu - (uint32_t)k);
 }
-__device__ __forceinline__ uint64_t wave_max_u64(uint64_t k) {
-#pragma unroll
-    for (int off = kWave / 2; off > 0; off >>= 1) {
-        uint64_t o = __shfl_xor(k, off, kWave);
-        k = o > k ? o : k;
+// a / b for a >= 0, b > 0: one 32-bit division when both fit in 32 bits (the
+// usual case for the slot counts and indices of a step), the 64-bit expansion
+// otherwise, which is several times longer on the GPU.
+__device__ __forceinline__ int64_t udiv64(int64_t a, int64_t b) {
+    if ((((uint64_t)a | (uint64_t)b) >> 32) == 0) return (int64_t)((uint32_t)a / (uint32_t)b);
+    return (int64_t)((uint64_t)a / (uint64_t)b);
+}
+
+// Largest u64 key over aligned groups of 2^lq lanes (lq <= 6), on every lane
+// of the group; the whole wave must be active. Groups of 2 and 4 exchange
+// through DPP quad permutes, of 8 and 16 through the half-row and row mirrors
+// (lane i of a group meets lane size-1-i, in the other half, once the halves
+// hold their own maxima), of 32 and 64 through LDS permutes. Four of the six
+// steps of a full wave then stay in the VALU (an LDS permute costs about 120
+// cycles).
+__device__ __forceinline__ uint64_t dpp_u64(uint64_t k, int ctrl_sel) {
+    const int lo = (int)(uint32_t)k, hi = (int)(uint32_t)(k >> 32);
+    int l2, h2;
+    switch (ctrl_sel) {
+    case 0:
+        l2 = __builtin_amdgcn_update_dpp(lo, lo, 0xB1, 0xF, 0xF, false);  // quad_perm [1,0,3,2]
+        h2 = __builtin_amdgcn_update_dpp(hi, hi, 0xB1, 0xF, 0xF, false);
+        break;
+    case 1:
+        l2 = __builtin_amdgcn_update_dpp(lo, lo, 0x4E, 0xF, 0xF, false);  // quad_perm [2,3,0,1]
+        h2 = __builtin_amdgcn_update_dpp(hi, hi, 0x4E, 0xF, 0xF, false);
+        break;
+    case 2:
+        l2 = __builtin_amdgcn_update_dpp(lo, lo, 0x141, 0xF, 0xF, false);  // row_half_mirror
+        h2 = __builtin_amdgcn_update_dpp(hi, hi, 0x141, 0xF, 0xF, false);
+        break;
+    default:
+        l2 = __builtin_amdgcn_update_dpp(lo, lo, 0x140, 0xF, 0xF, false);  // row_mirror
+        h2 = __builtin_amdgcn_update_dpp(hi, hi, 0x140, 0xF, 0xF, false);
+        break;
     }
+    return ((uint64_t)(uint32_t)h2 << 32) | (uint64_t)(uint32_t)l2;
+}
+__device__ __forceinline__ uint64_t group_max_u64(uint64_t k, int lq) {
+    uint64_t o;
+    if (lq > 0) { o = dpp_u64(k, 0); k = o > k ? o : k; }
+    if (lq > 1) { o = dpp_u64(k, 1); k = o > k ? o : k; }
+    if (lq > 2) { o = dpp_u64(k, 2); k = o > k ? o : k; }
+    if (lq > 3) { o = dpp_u64(k, 3); k = o > k ? o : k; }
+    if (lq > 4) { o = __shfl_xor(k, 16, kWave); k = o > k ? o : k; }
+    if (lq > 5) { o = __shfl_xor(k, 32, kWave); k = o > k ? o : k; }
     return k;
 }
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t k) { return group_max_u64(k, 6); }
 __device__ __forceinline__ float wave_sum_f32(float x) {
     // Butterfly: partners add the same two values, so every lane ends with the
     // same bit pattern and the order is fixed (deterministic).
@@ -86,13 +127,14 @@ __device__ __forceinline__ int64_t partition_q(int64_t E, int64_t W) {
 // ---------------------------------------------------- fused-step sub-chunks
 // The fused step streams a virtual array of E vector slots (rows laid end to
 // end) in sub-chunks of K slots, K = max(kSubMin, ceil(E / Wt)) for a target
-// wave count Wt: about one contiguous sub-chunk per wave. Sub-chunk s stores
-// the key of its segment inside row r at keys[s + r], collision-free as for
-// the balanced partition, with s < Wt <= kMaxWaves.
+// wave count Wt: about one contiguous sub-chunk per wave. The root rows'
+// sub-chunk s stores the key of its segment inside row r at rkeys[s + r],
+// collision-free as for the balanced partition, with s < Wt <= kMaxWaves; the
+// draft rows' segments merge into one key per row by atomic max.
 constexpr int64_t kSubMin = 1024;  // 16 KiB of bf16
 
 __device__ __forceinline__ int64_t sub_len(int64_t E, int64_t Wt) {
-    const int64_t k = (E + Wt - 1) / Wt;
+    const int64_t k = udiv64(E + Wt - 1, Wt);
     return k < kSubMin ? kSubMin : k;
 }
 
@@ -104,11 +146,15 @@ __device__ __forceinline__ int64_t sub_len(int64_t E, int64_t Wt) {
 //                                large enough for
 // rcnt:  uint64 [kMaxFusedB]     per-request arrival counters of the fused
 //                                step (zero between calls: each request's last
-//                                arriver resets its own)
+//                                arriver resets its own), spread so that
+//                                consecutive requests sit 128 bytes apart
 // acnt:  uint64 [kMaxFusedB]     per-request arrival counters of dspark_accept
 //                                (zero between calls: each request's last
 //                                arriver resets its own)
 // keys:  uint64 [kMaxWaves + B*(gamma+1)] argmax segment keys of packed rows
+//                                (dspark_accept); in the fused step, one key
+//                                per dense draft row (b*(gamma+1) + j), which
+//                                the request's front workgroup zeroes
 // rkeys: uint64 [kMaxWaves + B]  segment keys of the root rows (fused step)
 // surv:  float [B*gamma]         survival scratch (when the caller passes none)
 // conf:  float [B*gamma]         score scratch (when the caller passes none)

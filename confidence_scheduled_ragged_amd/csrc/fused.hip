@@ -10,9 +10,13 @@
 // raises a flag; every workgroup waits for it once, scans the lengths into
 // cu_seqlens in LDS, writes the schedule outputs of its own requests and
 // streams one contiguous sub-chunk of the draft rows. Root-row waves reach
-// the drafts later and get shorter sub-chunks. Per-request atomics count the
-// streamed slots of the root row and the drafts; the wave that completes a
-// request merges its keys and writes the acceptance and bonus token.
+// the drafts later and get shorter sub-chunks. Each row segment leaves its
+// argmax key in a slot of its own (zeroed by the request workgroups before
+// any is written); per-request atomics count the streamed slots of the root
+// row and the drafts, issued without waiting for the key stores; the wave
+// that completes a request reads the request's slots (polling any not yet
+// landed), its root keys and tokens in one memory round trip and writes the
+// acceptance and bonus token.
 //
 // Two launches:
 //   front   request workgroups as above and root workgroups; in budget mode
@@ -20,8 +24,8 @@
 //           the batch-wide top-T pick and writes every length.
 //   stream  every workgroup scans the lengths and writes its schedule
 //           outputs; the draft rows are cut into sub-chunks of about equal
-//           length, one contiguous run per wave, and the wave that completes
-//           a request's draft rows finishes it.
+//           length (at least 4 KiB), one contiguous run per wave, and the
+//           wave that completes a request's draft rows finishes it as above.
 //
 // Long contiguous runs per wave were measured faster than small interleaved
 // sub-chunks (HBM row-buffer locality), and two 16-byte loads in flight per
@@ -74,6 +78,22 @@ constexpr int kOneLaunchMinB = 96;
 constexpr int kOneGemvUnroll = 4;
 constexpr int kOneRootUnroll = 4;
 constexpr int kOneStreamUnroll = 2;
+// Short sub-chunks (at most kShortSub slots: small steps, where a wave's
+// sub-chunk is a chain of dependent load rounds rather than a share of the
+// bandwidth) are streamed with eight 16-byte loads in flight per lane, so
+// 16 KiB is two rounds instead of eight.
+constexpr int kStreamUnrollShort = 8;
+constexpr int64_t kShortSub = 4096;
+// Minimum sub-chunk of the fused step's root and draft rows: 4 KiB of bf16, one
+// load round of a wave at four 16-byte loads per lane. Small steps then spread
+// their few rows over many waves, each a single round trip (the finishing
+// wave reads a row's segment keys in parallel, so more segments cost no
+// extra round trips).
+constexpr int64_t kStepSubMin = 256;
+__device__ __forceinline__ int64_t step_sub_len(int64_t E, int64_t Wt) {
+    const int64_t k = udiv64(E + Wt - 1, Wt);
+    return k < kStepSubMin ? kStepSubMin : k;
+}
 constexpr double kLead = 0.70;
 constexpr int kRootUnrollShallow = 2;
 
@@ -88,6 +108,8 @@ struct FrontParams {
     float *conf, *surv;
     int32_t *lengths;
     uint64_t *rkeys;      // segment keys of the root rows
+    uint64_t *keys;       // draft segment keys; the request workgroups zero
+    int64_t key_words;    // words [0, key_words) of them before any is written
     uint64_t *req_arrivals;  // [B] the stream kernel's per-request counters, zeroed here
     unsigned *arrivals;   // budget select in the front kernel: arrival counter, else NULL
 };
@@ -102,13 +124,13 @@ __device__ __forceinline__ void front_root_rows(const FrontParams &p, int64_t w,
     const int lane = threadIdx.x & (kWave - 1);
     const int64_t Vv = kVec ? (p.V >> 3) : p.V;
     const int64_t E = (int64_t)p.B * Vv;
-    const int64_t K = sub_len(E, nwaves);
-    const int64_t NS = (E + K - 1) / K;
+    const int64_t K = step_sub_len(E, nwaves);
+    const int64_t NS = udiv64(E + K - 1, K);
     const size_t row_stride = (size_t)(p.gamma + 1) * (size_t)p.V;
     for (int64_t cur = w; cur < NS; cur += nwaves) {
         int64_t e = cur * K;
         const int64_t e_end = e + K < E ? e + K : E;
-        int64_t r = e / Vv;
+        int64_t r = udiv64(e, Vv);
         while (e < e_end) {
             const int64_t row_end = (r + 1) * Vv;
             const int64_t seg_end = e_end < row_end ? e_end : row_end;
@@ -135,11 +157,11 @@ __device__ __forceinline__ void front_root_rows(const FrontParams &p, int64_t w,
 template <typename F>
 __device__ __forceinline__ void root_segments(int64_t E, int64_t K, int64_t Vv, int64_t w,
                                               int64_t nwaves, F f) {
-    const int64_t NS = (E + K - 1) / K;
+    const int64_t NS = udiv64(E + K - 1, K);
     for (int64_t cur = w; cur < NS; cur += nwaves) {
         int64_t e = cur * K;
         const int64_t e_end = e + K < E ? e + K : E;
-        int64_t r = e / Vv;
+        int64_t r = udiv64(e, Vv);
         while (e < e_end) {
             const int64_t row_end = (r + 1) * Vv;
             const int64_t seg_end = e_end < row_end ? e_end : row_end;
@@ -179,6 +201,24 @@ __device__ __forceinline__ void front_request(const FrontParams &p, const uint16
         else
             p.lengths[b] = L;
     }
+}
+
+// Arrival counter of request b (b < kMaxFusedB) in the per-request counter
+// array: consecutive requests 128 bytes apart, so the atomics of different
+// requests do not queue on one cache line (a bijection of [0, 4096)).
+__device__ __forceinline__ uint64_t *req_counter(uint64_t *base, int b) {
+    static_assert(kMaxFusedB == 4096, "the counter spread assumes 4096 counters");
+    return base + ((b & 255) << 4) + (b >> 8);
+}
+
+// Part i of n of the draft segment keys set to zero by the calling workgroup.
+// The stores are device-coherent: a key written later by another workgroup
+// (another XCD) must never be overwritten by a zero left in an L2.
+__device__ __forceinline__ void zero_key_part(const FrontParams &p, int i, int n) {
+    const int64_t c = udiv64(p.key_words + n - 1, n);
+    const int64_t hi = (int64_t)(i + 1) * c < p.key_words ? (int64_t)(i + 1) * c : p.key_words;
+    for (int64_t k = (int64_t)i * c + threadIdx.x; k < hi; k += blockDim.x)
+        __hip_atomic_store(p.keys + k, (uint64_t)0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // Budget / combined: the batch-wide pick over every request's survival (read
@@ -227,7 +267,7 @@ __device__ __forceinline__ void front_pick(const FrontParams &p, float *sv, uint
     budget_lengths(sv, nullptr, p.B, p.gamma, cut, p.lengths, scan_lds);
 }
 
-template <bool kVecH, bool kLdsW, bool kVecV, int kRootUnroll>
+template <bool kVecH, bool kLdsW, bool kVecV, int kRootUnroll, int kGemvU = kGemvUnroll>
 __global__ __launch_bounds__(kFrontThreads) void step_front_kernel(FrontParams p) {
     extern __shared__ __align__(16) uint16_t dyn_lds[];
     __shared__ float z_s[DSPARK_MAX_GAMMA], p_s[DSPARK_MAX_GAMMA], s_s[DSPARK_MAX_GAMMA];
@@ -244,8 +284,9 @@ __global__ __launch_bounds__(kFrontThreads) void step_front_kernel(FrontParams p
     const int b = blockIdx.x;
     const int tid = threadIdx.x;
     if (tid == 0)
-        __hip_atomic_store(p.req_arrivals + b, (uint64_t)0, __ATOMIC_RELAXED,
+        __hip_atomic_store(req_counter(p.req_arrivals, b), (uint64_t)0, __ATOMIC_RELAXED,
                            __HIP_MEMORY_SCOPE_AGENT);
+    zero_key_part(p, b, p.B);
     const uint16_t *wp = p.w;
     if (kLdsW) {
         stage_w(p.w, p.d, dyn_lds);
@@ -254,7 +295,7 @@ __global__ __launch_bounds__(kFrontThreads) void step_front_kernel(FrontParams p
     }
     // the select reads survival from another workgroup of this grid
     const bool select_here = p.arrivals != nullptr;
-    front_request<kVecH>(p, wp, b, select_here, false, z_s, p_s, s_s);
+    front_request<kVecH, kGemvU>(p, wp, b, select_here, false, z_s, p_s, s_s);
     if (!select_here) return;
 
     // budget: count this request as done once its survival stores are complete;
@@ -280,23 +321,34 @@ struct StreamParams {
     const int32_t *lengths;
     int B, gamma, V;
     int32_t *cu, *ptok, *psrc, *pam, *acc, *bonus;
-    uint64_t *keys;
+    uint64_t *keys;         // draft segment keys, keys[s + r] (zero at the start)
     const uint64_t *rkeys;  // root-row keys
     uint64_t *arrivals;     // [B] streamed slots per request (zero between calls)
     int target_waves;       // sub-chunk length: about one sub-chunk per target wave
     int root_waves;         // waves that streamed the root rows
+    unsigned *timed_out;    // sticky: set when a wait for a key gave up
+    unsigned long long wait_ticks;  // bound of such a wait, in 100 MHz clock ticks
 };
 
 // Largest b in [0, B] with cu[b] - b <= r, i.e. the request that owns draft
-// row r (draft rows start at cu[b] - b; requests without drafts own none)
-// when r < cu[B] - B.
-__device__ __forceinline__ int draft_owner(const int *cu, int B, int64_t r) {
-    int lo = 0, hi = B;
-    while (lo < hi) {
-        const int mid = (lo + hi + 1) >> 1;
-        if ((int64_t)(cu[mid] - mid) <= r) lo = mid; else hi = mid - 1;
+// row r (draft rows start at cu[b] - b, which never falls as b rises;
+// requests without drafts own none) when 0 <= r < cu[B] - B. A whole wave
+// searches: each round the 64 lanes test 64 evenly spaced candidates of the
+// remaining range at once (one LDS read and a ballot), so B = 4096 takes
+// three rounds instead of twelve dependent reads.
+__device__ __forceinline__ int wave_draft_owner(const int *cu, int B, int64_t r) {
+    const int lane = threadIdx.x & (kWave - 1);
+    int lo = 0, hi = B;  // cu[lo] - lo <= r holds throughout
+    while (true) {
+        const int step = (hi - lo + kWave) / kWave;  // ceil((hi - lo + 1) / 64)
+        const int idx = lo + lane * step;
+        const bool ok = idx <= hi && (int64_t)(cu[idx] - idx) <= r;
+        const uint64_t m = __ballot(ok);  // lane 0 always set
+        const int at = lo + (63 - __clzll((long long)m)) * step;
+        if (step == 1) return at;
+        lo = at;
+        hi = at + step - 1 < hi ? at + step - 1 : hi;
     }
-    return lo;
 }
 
 // Verify lengths (clamped to [0, gamma]) and cu_seqlens into LDS. Every thread
@@ -343,13 +395,16 @@ __device__ __forceinline__ void write_schedule(const StreamParams &p, const int 
     }
 }
 
-// Counts n more streamed slots of a request on its arrival counter once the
-// calling wave's key stores are complete. True on the wave whose count
-// reaches `target` (the request's last contribution); that wave also returns
-// the counter to zero for the next call. Called by a whole wave; no waiting.
+// Counts n more streamed slots of a request on its arrival counter. True on
+// the wave whose count reaches `target` (the request's last contribution);
+// that wave also returns the counter to zero for the next call. kAfterStores:
+// count only once the calling wave's stores are at the coherence point (root
+// keys, which are read without a check); draft segment keys need no wait, as
+// the finishing wave polls each until it is set. Called by a whole wave.
+template <bool kAfterStores>
 __device__ __forceinline__ bool arrive_last(uint64_t *cnt, int64_t n, int64_t target) {
     const int lane = threadIdx.x & (kWave - 1);
-    __builtin_amdgcn_s_waitcnt(0);  // the key stores are at the coherence point
+    if (kAfterStores) __builtin_amdgcn_s_waitcnt(0);
     unsigned long long old = 0;
     if (lane == 0)
         old = __hip_atomic_fetch_add(cnt, (uint64_t)n, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -360,45 +415,161 @@ __device__ __forceinline__ bool arrive_last(uint64_t *cnt, int64_t n, int64_t ta
     return last;
 }
 
-// Acceptance and bonus of request b by the calling wave: the root row's
-// argmax from the root keys (kRootCoherent: written by this same grid), the
-// draft rows' from the draft keys of sub-chunk length K.
-template <bool kRootCoherent>
-__device__ __forceinline__ void accept_request(const StreamParams &p, const int *len_s,
-                                               const int *cu_s, int b, int64_t Vv, int64_t K,
-                                               int64_t Kr) {
-    const int start = cu_s[b];
-    const int dstart = start - b;  // first draft row of request b
-    wave_accept_rows(
-        [&](int j) {
-            return j == 0 ? row_argmax<kRootCoherent>(p.rkeys, b, Vv, Kr)
-                          : row_argmax<true>(p.keys, dstart + j - 1, Vv, K);
-        },
-        len_s[b] + 1, p.gamma, p.tokens + (size_t)b * (p.gamma + 1), p.pam + start, p.acc + b,
-        p.bonus + b);
+// Draft segment key at k, as already loaded (x), polled until it is set: its
+// wave stores it before it counts its slots, so once a request's count is
+// complete every key of it is on its way. A wait beyond wait_ticks sets the
+// sticky time-out flag and gives 0 ("no element").
+__device__ __forceinline__ uint64_t settled_key(const StreamParams &p, const uint64_t *k,
+                                                uint64_t x) {
+    if (x != 0) return x;
+    const unsigned long long t0 = wall_clock64();
+    while ((x = load_key_coherent(k)) == 0) {
+        if (wall_clock64() - t0 > p.wait_ticks) {
+            __hip_atomic_store(p.timed_out, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            break;
+        }
+        __builtin_amdgcn_s_sleep(1);
+    }
+    return x;
+}
+
+constexpr int kFinBatch = 8;  // segment keys in flight per lane in the finisher
+
+// Largest segment key of packed draft row r, whose segments are those of
+// sub-chunks sf..sl (sub(e): the sub-chunk of slot e), kept at keys[s + r]; the
+// calling lane reads segments t0, t0 + Q, ..., kFinBatch loads at a time.
+template <typename Sub>
+__device__ __forceinline__ uint64_t draft_row_key(const StreamParams &p, int64_t r, int64_t Vv,
+                                                  Sub sub, int t0, int Q) {
+    const int64_t sf = sub(r * Vv);
+    const int64_t cnt = sub((r + 1) * Vv - 1) - sf + 1;
+    const uint64_t *base = p.keys + sf + r;
+    uint64_t k = 0;
+    for (int64_t t = t0; t < cnt; t += (int64_t)kFinBatch * Q) {
+        uint64_t x[kFinBatch];
+#pragma unroll
+        for (int u = 0; u < kFinBatch; ++u) {
+            const int64_t tu = t + (int64_t)u * Q;
+            x[u] = load_key_coherent(base + (tu < cnt ? tu : t));  // in range; repeats unused
+        }
+#pragma unroll
+        for (int u = 0; u < kFinBatch; ++u)
+            if (t + (int64_t)u * Q < cnt) {
+                const uint64_t y = settled_key(p, base + t + (int64_t)u * Q, x[u]);
+                k = y > k ? y : k;
+            }
+    }
+    return k;
+}
+
+// Acceptance and bonus of request b by the calling wave (a whole wave), once
+// all its slots are counted: the root row's argmax from its segment keys
+// (sub-chunks of Kr slots; kRootCoherent: written by this same grid), each
+// draft row's from its segment keys. For requests of fewer than 64 draft rows
+// the draft keys, the root keys and the draft tokens are all loaded before any
+// is waited for (one memory round trip): Q lanes per draft row (a power of
+// two, Q * L <= 64) read the row's segment keys and reduce them by butterfly
+// within their group.
+// What the finishing wave of request b needs besides the draft keys, loaded
+// when a wave starts on the request so that it has arrived by the time the
+// wave may finish it: draft token lane + 1 (lanes below L_b) and, with kRoot
+// (the root keys are final: written by an earlier launch), each lane's first
+// root segment key. kRootCoherent: the root keys were written by this grid.
+struct ReqPre {
+    uint64_t xr;
+    int32_t tk;
+};
+template <bool kRoot, bool kRootCoherent>
+__device__ __forceinline__ ReqPre prefetch_request(const StreamParams &p, int b, int L, int64_t Vv,
+                                                   int64_t Kr) {
+    const int lane = threadIdx.x & (kWave - 1);
+    ReqPre q;
+    q.xr = 0;
+    q.tk = 0;
+    if (kRoot) {
+        const int64_t s = udiv64(b * Vv, Kr) + lane;
+        if (s <= udiv64((b + 1) * Vv - 1, Kr))
+            q.xr = kRootCoherent ? load_key_coherent(p.rkeys + b + s) : p.rkeys[b + s];
+    }
+    if (lane < L) q.tk = p.tokens[(size_t)b * (p.gamma + 1) + lane + 1];
+    return q;
+}
+
+template <bool kRootCoherent, bool kPreRoot, typename Sub>
+__device__ __forceinline__ void finish_request(const StreamParams &p, const int *len_s,
+                                               const int *cu_s, int b, int64_t Vv, int64_t Kr,
+                                               Sub sub, const ReqPre &pre) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const int L = len_s[b];
+    const int64_t r0 = cu_s[b] - b;  // first packed draft row of b
+    const int32_t *tok = p.tokens + (size_t)b * (p.gamma + 1);
+    int32_t *pam_b = p.pam + cu_s[b];
+    // root keys: each lane's first one (prefetched, or loaded now and reduced
+    // later), then any further ones
+    const int64_t s_lo = udiv64(b * Vv, Kr), s_hi = udiv64((b + 1) * Vv - 1, Kr);
+    const uint64_t *rk = p.rkeys + b;
+    uint64_t xr = pre.xr;
+    if (!kPreRoot && s_lo + lane <= s_hi)
+        xr = kRootCoherent ? load_key_coherent(rk + s_lo + lane) : rk[s_lo + lane];
+    if (L < kWave) {
+        const int32_t tk = pre.tk;
+        const int lq = L > 0 ? 31 - __builtin_clz(kWave / L) : 6;  // log2 Q
+        const int Q = 1 << lq;
+        const int j = lane >> lq;
+        uint64_t k = j < L ? draft_row_key(p, r0 + j, Vv, sub, lane & (Q - 1), Q) : 0ull;
+        for (int64_t s = s_lo + lane + kWave; s <= s_hi; s += kWave) {
+            const uint64_t x = kRootCoherent ? load_key_coherent(rk + s) : rk[s];
+            xr = x > xr ? x : xr;
+        }
+        const int32_t root = key_index(wave_max_u64(xr));
+        k = group_max_u64(k, lq);
+        // lane j >= 1 takes draft row j - 1's key from the first lane of its group
+        const uint64_t dk = __shfl(k, lane >= 1 && lane <= L ? (lane - 1) << lq : 0, kWave);
+        wave_accept_rows_t([&](int jj) { return jj == 0 ? root : key_index(dk); },
+                           [&](int) { return tk; }, L + 1, p.gamma, pam_b, p.acc + b,
+                           p.bonus + b);
+    } else {
+        for (int64_t s = s_lo + lane + kWave; s <= s_hi; s += kWave) {
+            const uint64_t x = kRootCoherent ? load_key_coherent(rk + s) : rk[s];
+            xr = x > xr ? x : xr;
+        }
+        const int32_t root = key_index(wave_max_u64(xr));
+        wave_accept_rows(
+            [&](int jj) {
+                return jj == 0 ? root : key_index(draft_row_key(p, r0 + jj - 1, Vv, sub, 0, 1));
+            },
+            L + 1, p.gamma, tok, pam_b, p.acc + b, p.bonus + b);
+    }
 }
 
 // Slots [e, e_end) of the draft rows of all requests laid end to end (Vv
 // slots per row), streamed by the calling wave as sub-chunk s: each row
-// segment leaves one key at keys[s + r]; arrive(b, n) counts the n slots of
-// request b streamed, once at each change of request and at the end.
-template <bool kVec, int kUnroll, typename Arrive>
+// segment leaves its key at keys[s + r] (s + r rises by one at every sub-chunk
+// or row boundary, so no two segments share a key, and a row's segments have
+// consecutive keys); arrive(b, n) counts the n slots of request b streamed,
+// once at each change of request and at the end, with what the request's
+// finishing wave needs (prefetch_request<kPreRoot, kRootCoherent>, root
+// sub-chunks of Kr slots), loaded when the wave starts on the request.
+template <bool kVec, int kUnroll, bool kPreRoot, bool kRootCoherent, typename Arrive>
 __device__ __forceinline__ void stream_draft_span(const StreamParams &p, const int *cu_s,
-                                                  int64_t Vv, int64_t s, int64_t e, int64_t e_end,
-                                                  Arrive arrive) {
+                                                  int64_t Vv, int64_t Kr, int64_t s, int64_t e,
+                                                  int64_t e_end, Arrive arrive) {
     const int lane = threadIdx.x & (kWave - 1);
     const int g1 = p.gamma + 1;
-    int64_t r = e / Vv;
+    int64_t r = udiv64(e, Vv);
     int cur_b = -1;    // request of the rows being streamed
     int64_t done = 0;  // its slots streamed in this sub-chunk
+    ReqPre pre;
+    int b = e < e_end ? wave_draft_owner(cu_s, p.B, r) : 0;
     while (e < e_end) {
         const int64_t row_end = (r + 1) * Vv;
         const int64_t seg_end = e_end < row_end ? e_end : row_end;
-        const int b = draft_owner(cu_s, p.B, r);
+        while (b < p.B && (int64_t)(cu_s[b + 1] - (b + 1)) <= r) ++b;
         if (b != cur_b) {
-            if (cur_b >= 0) arrive(cur_b, done);
+            if (cur_b >= 0) arrive(cur_b, done, pre);
             cur_b = b;
             done = 0;
+            pre = prefetch_request<kPreRoot, kRootCoherent>(p, b, cu_s[b + 1] - cu_s[b] - 1, Vv, Kr);
         }
         const int64_t src = (int64_t)b * g1 + 1 + (r - (cu_s[b] - b));
         float best = -INFINITY;
@@ -412,7 +583,7 @@ __device__ __forceinline__ void stream_draft_span(const StreamParams &p, const i
         e = seg_end;
         ++r;
     }
-    if (cur_b >= 0) arrive(cur_b, done);
+    if (cur_b >= 0) arrive(cur_b, done, pre);
 }
 
 // The draft rows (E slots) in sub-chunks of K slots dealt cyclically: wave w
@@ -420,12 +591,18 @@ __device__ __forceinline__ void stream_draft_span(const StreamParams &p, const i
 // HBM row buffers better used than many short interleaved ones.
 template <bool kVec, typename Arrive>
 __device__ __forceinline__ void stream_draft_rows(const StreamParams &p, const int *cu_s,
-                                                  int64_t Vv, int64_t E, int64_t K, int64_t w,
-                                                  int64_t W, Arrive arrive) {
-    const int64_t NS = (E + K - 1) / K;
-    for (int64_t cur = w; cur < NS; cur += W)
-        stream_draft_span<kVec, kStreamUnroll>(p, cu_s, Vv, cur, cur * K,
-                                               cur * K + K < E ? cur * K + K : E, arrive);
+                                                  int64_t Vv, int64_t Kr, int64_t E, int64_t K,
+                                                  int64_t w, int64_t W, Arrive arrive) {
+    const int64_t NS = udiv64(E + K - 1, K);
+    for (int64_t cur = w; cur < NS; cur += W) {
+        const int64_t e0 = cur * K, e1 = cur * K + K < E ? cur * K + K : E;
+        if (K <= kShortSub)
+            stream_draft_span<kVec, kStreamUnrollShort, true, false>(p, cu_s, Vv, Kr, cur, e0, e1,
+                                                                     arrive);
+        else
+            stream_draft_span<kVec, kStreamUnroll, true, false>(p, cu_s, Vv, Kr, cur, e0, e1,
+                                                                arrive);
+    }
 }
 
 template <bool kVec>
@@ -442,17 +619,22 @@ __global__ __launch_bounds__(kStreamThreads) void step_stream_kernel(StreamParam
 
     const int64_t Vv = kVec ? (p.V >> 3) : p.V;
     const int64_t E = (int64_t)(cu_s[B] - B) * Vv;
-    const int64_t K = sub_len(E, p.target_waves);
-    const int64_t Kr = sub_len((int64_t)B * Vv, p.root_waves);
+    const int64_t K = step_sub_len(E, p.target_waves);
+    const int64_t Kr = step_sub_len((int64_t)B * Vv, p.root_waves);
+    auto sub = [&](int64_t e) { return udiv64(e, K); };
     // requests without draft rows are finished by the workgroup that owns them
     if (tid < kWave)
         for (int b = blockIdx.x; b < B; b += gridDim.x)
-            if (len_s[b] == 0) accept_request<false>(p, len_s, cu_s, b, Vv, K, Kr);
+            if (len_s[b] == 0)
+                finish_request<false, true>(p, len_s, cu_s, b, Vv, Kr, sub,
+                                            prefetch_request<true, false>(p, b, 0, Vv, Kr));
     // the wave that completes a request's draft rows finishes it
-    stream_draft_rows<kVec>(p, cu_s, Vv, E, K, (int64_t)blockIdx.x * nw + tid / kWave,
-                            (int64_t)gridDim.x * nw, [&](int b, int64_t n) {
-                                if (arrive_last(p.arrivals + b, n, (int64_t)len_s[b] * Vv))
-                                    accept_request<false>(p, len_s, cu_s, b, Vv, K, Kr);
+    stream_draft_rows<kVec>(p, cu_s, Vv, Kr, E, K, (int64_t)blockIdx.x * nw + tid / kWave,
+                            (int64_t)gridDim.x * nw, [&](int b, int64_t n, const ReqPre &pre) {
+                                if (arrive_last<false>(req_counter(p.arrivals, b), n,
+                                                       (int64_t)len_s[b] * Vv))
+                                    finish_request<false, true>(p, len_s, cu_s, b, Vv, Kr, sub,
+                                                                pre);
                             });
 }
 
@@ -493,21 +675,29 @@ struct OneParams {
 // sub-chunk per wave in two regions: the first NA sub-chunks, of KA slots, go
 // to the early waves (request and plain stream workgroups, free once the
 // lengths are final), the others, of KB = KA - lead slots, to the root-row
-// waves, which reach the drafts later. Sub-chunk s keeps the key of its
-// segment inside row r at keys[s + r]: s + r still rises by one at every
-// sub-chunk or row boundary, so no two segments share a key.
+// waves, which reach the drafts later. When the root waves' share would be
+// below the minimum length, the early waves take no more than covers the
+// drafts (at least the minimum, at most the minimum plus the lead): a longer
+// sub-chunk would only lengthen their chains.
 struct SplitLayout {
     int64_t KA, KB, EA, NA, E;
     __device__ __forceinline__ SplitLayout(int64_t E_, int64_t WA, int64_t W, int64_t lead) {
         E = E_;
         const int64_t kb = (E - WA * lead + W - 1) / W;
-        KB = kb < kSubMin ? kSubMin : kb;
-        KA = KB + lead;
+        if (kb < kStepSubMin) {
+            KB = kStepSubMin;
+            const int64_t ka = udiv64(E + WA - 1, WA);
+            KA = ka < kStepSubMin ? kStepSubMin : (ka > kStepSubMin + lead ? kStepSubMin + lead : ka);
+        } else {
+            KB = kb;
+            KA = KB + lead;
+        }
         EA = WA * KA < E ? WA * KA : E;
-        NA = (EA + KA - 1) / KA;
+        NA = udiv64(EA + KA - 1, KA);
     }
+    // sub-chunk of slot e < E
     __device__ __forceinline__ int64_t sub(int64_t e) const {
-        return e < EA ? e / KA : NA + (e - EA) / KB;
+        return e < EA ? udiv64(e, KA) : NA + udiv64(e - EA, KB);
     }
     // slots of sub-chunk s: [*e0, *e1), empty past the end
     __device__ __forceinline__ void span(int64_t s, int64_t *e0, int64_t *e1) const {
@@ -546,17 +736,19 @@ __global__ __launch_bounds__(kFrontThreads) void step_one_kernel(OneParams q) {
     const bool is_root = wg >= q.gemv_wgs && wg < q.gemv_wgs + q.root_wgs;
     bool wait = true;
     if (wg < q.gemv_wgs) {
+        zero_key_part(p, wg, q.gemv_wgs);
         for (int b = wg; b < B; b += q.gemv_wgs) {
             // the request's arrival counter starts this call at zero (streaming
             // waves only add to it after the go word)
             if (tid == 0)
-                __hip_atomic_store(sp.arrivals + b, (uint64_t)0, __ATOMIC_RELAXED,
+                __hip_atomic_store(req_counter(sp.arrivals, b), (uint64_t)0, __ATOMIC_RELAXED,
                                    __HIP_MEMORY_SCOPE_AGENT);
             front_request<kVecH, kOneGemvUnroll>(p, p.w, b, false, true, z_s, p_s, s_s);
             __syncthreads();
         }
-        // this workgroup's length and counter stores are at the coherence
-        // point: count it; the last to count lets every workgroup go on
+        // this workgroup's length, counter and key stores are at the
+        // coherence point: count it; the last to count lets every workgroup go
+        // on
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
         if (tid == 0) {
@@ -606,35 +798,37 @@ __global__ __launch_bounds__(kFrontThreads) void step_one_kernel(OneParams q) {
     const int64_t dw = is_root ? WA + (int64_t)(wg - q.gemv_wgs) * nw + wave
                                : (int64_t)(wg < q.gemv_wgs ? wg : wg - q.root_wgs) * nw + wave;
     const SplitLayout lay((int64_t)(cu_s[B] - B) * Vv, WA, (int64_t)G * nw, q.lead);
-    const int64_t Kr = sub_len((int64_t)B * Vv, root_waves);
+    const int64_t Kr = step_sub_len((int64_t)B * Vv, root_waves);
     // a request counts its root row and its draft rows; the wave that brings
     // the last of them finishes it: the root row's argmax from the root keys,
     // the draft rows' from the draft keys
-    auto arrive = [&](int b, int64_t n) {
-        if (!arrive_last(sp.arrivals + b, n, (int64_t)(len_s[b] + 1) * Vv)) return;
-        const int start = cu_s[b];
-        const int dstart = start - b;  // first draft row of request b
-        wave_accept_rows(
-            [&](int j) {
-                if (j == 0) return row_argmax<true>(sp.rkeys, b, Vv, Kr);
-                const int64_t r = dstart + j - 1;
-                return segment_keys_argmax<true>(sp.keys, r, lay.sub(r * Vv),
-                                                 lay.sub((r + 1) * Vv - 1));
-            },
-            len_s[b] + 1, sp.gamma, sp.tokens + (size_t)b * (sp.gamma + 1), sp.pam + start,
-            sp.acc + b, sp.bonus + b);
+    auto sub = [&](int64_t e) { return lay.sub(e); };
+    auto arrive_root = [&](int b, int64_t n) {
+        if (arrive_last<true>(req_counter(sp.arrivals, b), n, (int64_t)(len_s[b] + 1) * Vv))
+            finish_request<true, false>(sp, len_s, cu_s, b, Vv, Kr, sub,
+                                        prefetch_request<false, true>(sp, b, len_s[b], Vv, Kr));
+    };
+    // the root keys are final only once the request's count is complete: the
+    // draft waves prefetch the tokens only
+    auto arrive = [&](int b, int64_t n, const ReqPre &pre) {
+        if (arrive_last<false>(req_counter(sp.arrivals, b), n, (int64_t)(len_s[b] + 1) * Vv))
+            finish_request<true, false>(sp, len_s, cu_s, b, Vv, Kr, sub, pre);
     };
     if (is_root)
         root_segments((int64_t)B * Vv, Kr, Vv, (int64_t)(wg - q.gemv_wgs) * nw + wave, root_waves,
-                      arrive);
+                      arrive_root);
     // this wave's sub-chunk: early wave dw < WA takes region A's sub-chunk dw,
     // root wave dw takes region B's sub-chunk dw - WA
     const int64_t s_mine = dw < WA ? (dw < lay.NA ? dw : -1) : lay.NA + (dw - WA);
     if (s_mine >= 0) {
         int64_t e0, e1;
         lay.span(s_mine, &e0, &e1);
-        if (e0 < e1)
-            stream_draft_span<kVecV, kOneStreamUnroll>(sp, cu_s, Vv, s_mine, e0, e1, arrive);
+        if (e1 - e0 > 0 && e1 - e0 <= kShortSub)
+            stream_draft_span<kVecV, kStreamUnrollShort, false, true>(sp, cu_s, Vv, Kr, s_mine, e0,
+                                                                      e1, arrive);
+        else if (e0 < e1)
+            stream_draft_span<kVecV, kOneStreamUnroll, false, true>(sp, cu_s, Vv, Kr, s_mine, e0,
+                                                                    e1, arrive);
     }
     // every wave of this workgroup is past the wait: it leaves
     if (tid == 0) __hip_atomic_fetch_sub(q.go, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -663,11 +857,20 @@ static int stream_grid(size_t lds) {
     return gsz;
 }
 
+// Front grids of at most one workgroup per CU (small batches) take the head
+// from global memory (no staging round trip) and eight 16-byte hidden loads in
+// flight per lane: a request's GEMV is then one load round per wave. Their
+// occupancy (three waves per SIMD) still holds one workgroup per CU.
+constexpr int kGemvUnrollSmall = 8;
+
 template <bool kVecV, int kRootUnroll>
 static void launch_front_u(bool hvec, bool ldsw, const FrontParams &fp, int root_wgs, size_t lds,
                            hipStream_t s) {
     const dim3 grid(fp.B + root_wgs), block(kFrontThreads);
-    if (hvec && ldsw)
+    if (hvec && fp.B + root_wgs <= device_cu_count())
+        hipLaunchKernelGGL((step_front_kernel<true, false, kVecV, kRootUnroll, kGemvUnrollSmall>),
+                           grid, block, lds, s, fp);
+    else if (hvec && ldsw)
         hipLaunchKernelGGL((step_front_kernel<true, true, kVecV, kRootUnroll>), grid, block, lds, s,
                            fp);
     else if (hvec)
@@ -766,6 +969,7 @@ hipError_t launch_fused_step(const uint16_t *hidden, const uint16_t *w, float bi
     fp.surv = surv;
     fp.lengths = lengths;
     fp.rkeys = rkeys;
+    fp.keys = keys;
     fp.req_arrivals = rcnt;
     fp.arrivals = select_in_front ? arrivals : nullptr;
     size_t front_lds = ldsw ? (size_t)d * 2 : 0;
@@ -775,9 +979,13 @@ hipError_t launch_fused_step(const uint16_t *hidden, const uint16_t *w, float bi
     const int cus = device_cu_count();
     const int64_t Vv = vvec ? V / 8 : V;
     const int64_t root_min_wgs =
-        ((int64_t)B * Vv + kSubMin * (kFrontThreads / kWave) - 1) / (kSubMin * (kFrontThreads / kWave));
+        ((int64_t)B * Vv + kStepSubMin * (kFrontThreads / kWave) - 1) /
+        (kStepSubMin * (kFrontThreads / kWave));
     int64_t root_wgs = (int64_t)kFrontRootWGsPerCU * cus;
     root_wgs = root_wgs < root_min_wgs ? root_wgs : root_min_wgs;
+    // small batches keep the whole front grid at one workgroup per CU, where
+    // the front takes its small-grid variant
+    if (2 * B <= cus && root_wgs > cus - B) root_wgs = cus - B;
     if (root_wgs * (kFrontThreads / kWave) > kMaxWaves) root_wgs = kMaxWaves / (kFrontThreads / kWave);
     root_wgs = root_wgs < 1 ? 1 : root_wgs;
     const int root_waves = (int)root_wgs * (kFrontThreads / kWave);
@@ -800,11 +1008,16 @@ hipError_t launch_fused_step(const uint16_t *hidden, const uint16_t *w, float bi
     p.arrivals = rcnt;
     p.target_waves = kStreamWavesPerCU * cus < kMaxWaves ? kStreamWavesPerCU * cus : (int)kMaxWaves;
     p.root_waves = root_waves;
+    p.timed_out = reinterpret_cast<unsigned *>(wsb + ws_ctrl_offset() + kCtrlTimedOutOffset);
+    p.wait_ticks = wait_ticks ? wait_ticks : kWaitTicks;
+    // draft segment keys in use: keys[s + r] with s below the sub-chunk count
+    // (at most the target waves) and r below the draft rows (B * gamma)
+    fp.key_words = (int64_t)p.target_waves + (int64_t)B * gamma;
     // stream workgroups: enough for the target waves, and no more than the
     // largest possible draft rows (every request at gamma) fill with
     // minimum-length sub-chunks
     int stream_wgs_needed = (p.target_waves + kStreamThreads / kWave - 1) / (kStreamThreads / kWave);
-    const int64_t max_sub = ((int64_t)B * gamma * Vv + kSubMin - 1) / kSubMin;
+    const int64_t max_sub = ((int64_t)B * gamma * Vv + kStepSubMin - 1) / kStepSubMin;
     const int64_t max_wgs = (max_sub + kStreamThreads / kWave - 1) / (kStreamThreads / kWave);
     if (max_wgs < stream_wgs_needed) stream_wgs_needed = max_wgs < 1 ? 1 : (int)max_wgs;
 
@@ -827,6 +1040,8 @@ hipError_t launch_fused_step(const uint16_t *hidden, const uint16_t *w, float bi
         q.lead = (int64_t)(kLead * (double)((int64_t)B * Vv / root_waves));
         int grid = q.gemv_wgs + q.root_wgs;
         if (grid < stream_wgs_needed) grid = stream_wgs_needed;
+        // one sub-chunk per wave of the grid
+        q.f.key_words = (int64_t)grid * (kFrontThreads / kWave) + (int64_t)B * gamma;
         const size_t lds = (size_t)(2 * B + 1) * 4;
         if ((int64_t)grid * (kFrontThreads / kWave) <= kMaxWaves) {
             bool done = false;

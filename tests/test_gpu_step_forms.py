@@ -53,7 +53,8 @@ def _fresh_ws(cfg):
 
 
 def _counters_zero(ws, B):
-    head = ws[: CTRL_BYTES + 8 * min(B, MAX_FUSED_B)].cpu().numpy()
+    # the control words and every per-request counter (spread over the array)
+    head = ws[: CTRL_BYTES + 8 * MAX_FUSED_B].cpu().numpy()
     return int(np.count_nonzero(head)) == 0
 
 
