@@ -350,10 +350,15 @@ def run_gather(cfg, outs, steps, dspark, torch, width=7168):
                 frac_of_hbm_peak=nbytes / (us / 1e6) / 1e9 / HBM_PEAK_GBS)
 
 
-def run_graph_latency(cfg, steps, dspark, torch, make_step, make_params, R=4):
-    """Launch latency of the fused step at a small workload: K eager
-    dspark_step calls through the Python binding against K replays of HIP
-    graphs captured once per resident batch (same kernels, same buffers)."""
+def run_graph_latency(cfg, steps, dspark, torch, make_step, make_params, R=4, M=8):
+    """Latency of the fused step at a small workload, the same kernels and
+    buffers launched five ways: K eager dspark_step calls through the checked
+    binding; K calls of BoundStep objects (arguments checked and marshalled
+    once); K replays of HIP graphs holding one step each, captured once per
+    resident batch; and K/M replays of one graph holding M consecutive steps
+    (a step's cost as part of a larger captured graph, as in a serving loop
+    that captures the whole decode step). The difference between the last two
+    is the fixed cost of one graph launch."""
     dev = torch.device("cuda:0")
     p = make_params(cfg)
     slots = [make_step(cfg, i, device=dev, params=p) for i in range(R)]
@@ -365,20 +370,30 @@ def run_graph_latency(cfg, steps, dspark, torch, make_step, make_params, R=4):
         dspark.dspark_step(s.hidden, s.w, s.bias, s.temps, s.tokens, s.logits, cfg.mode,
                            cutoff=s.cutoff, budget=s.budget, out=outs[i], ws=ws)
 
-    def timed(fn):
+    def timed(fn, n=steps, per=1):
+        # wall and event time per step, and the host time to issue the calls
+        # (equal to the wall time when the host, not the GPU, sets the pace)
         for i in range(2 * R):
             fn(i % R)
         torch.cuda.synchronize()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         t0 = time.perf_counter()
         e0.record()
-        for i in range(steps):
+        for i in range(n):
             fn(i % R)
+        t1 = time.perf_counter()
         e1.record()
         torch.cuda.synchronize()
-        return (time.perf_counter() - t0) * 1e6 / steps, e0.elapsed_time(e1) * 1e3 / steps
+        issue.append((t1 - t0) * 1e6 / (n * per))
+        return ((time.perf_counter() - t0) * 1e6 / (n * per),
+                e0.elapsed_time(e1) * 1e3 / (n * per))
 
+    issue = []
     eager_wall, eager_ev = timed(body)
+    bound = [dspark.bind_step(s.hidden, s.w, s.bias, s.temps, s.tokens, s.logits, cfg.mode,
+                              cutoff=s.cutoff, budget=s.budget, out=outs[i], ws=ws)
+             for i, s in enumerate(slots)]
+    bound_wall, bound_ev = timed(lambda i: bound[i]())
     totals = [int(o["cu_seqlens"][-1].item()) for o in outs]
     nbytes = sum(step_bytes(cfg, t) for t in totals) / len(totals)
     side = torch.cuda.Stream()
@@ -397,10 +412,22 @@ def run_graph_latency(cfg, steps, dspark, torch, make_step, make_params, R=4):
     torch.cuda.synchronize()
     graph_wall, graph_ev = timed(lambda i: graphs[i].replay())
     del graphs
-    best = min(eager_ev, graph_ev)
+    gm = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(gm):
+        for i in range(M):
+            body(i % R)
+    torch.cuda.synchronize()
+    gm_wall, gm_ev = timed(lambda i: gm.replay(), n=max(1, steps // M), per=M)
+    del gm
+    best = min(bound_ev, gm_ev)
     return dict(workload=cfg.name, B=cfg.B, eager_us_per_step=eager_wall,
-                eager_event_us_per_step=eager_ev, graph_us_per_step=graph_wall,
-                graph_event_us_per_step=graph_ev, mean_packed_rows=sum(totals) / len(totals),
+                eager_event_us_per_step=eager_ev, bound_us_per_step=bound_wall,
+                bound_event_us_per_step=bound_ev, graph_us_per_step=graph_wall,
+                graph_event_us_per_step=graph_ev, steps_per_graph=M,
+                graph_multi_us_per_step=gm_wall, graph_multi_event_us_per_step=gm_ev,
+                graph_launch_cost_us=graph_ev - gm_ev,
+                host_issue_us_per_step=dict(zip(("eager", "bound", "graph", "graph_multi"), issue)),
+                mean_packed_rows=sum(totals) / len(totals),
                 algorithmic_bytes_per_step=nbytes,
                 achieved_gbs=nbytes / (best / 1e6) / 1e9,
                 frac_of_hbm_peak=nbytes / (best / 1e6) / 1e9 / HBM_PEAK_GBS)
@@ -701,7 +728,10 @@ def main():
         extra["graph_replay_latency"] = lat
         for x in lat:
             log(f"graph replay, {x['workload']}: eager {x['eager_us_per_step']:.1f} us/step, "
-                f"graph {x['graph_us_per_step']:.1f} us/step")
+                f"bound {x['bound_us_per_step']:.1f}, graph {x['graph_us_per_step']:.1f}, "
+                f"{x['steps_per_graph']} steps per graph {x['graph_multi_us_per_step']:.1f} "
+                f"(one graph launch {x['graph_launch_cost_us']:.1f} us); host issue per step "
+                + ", ".join(f"{k} {v:.1f}" for k, v in x["host_issue_us_per_step"].items()))
         context = stream_read_context(torch, dev)
         log(f"plain device copy: {context['gbs']:.0f} GB/s")
 

@@ -387,6 +387,19 @@ def dspark_step(hidden, w, bias, temps, tokens, logits, mode, cutoff=None, budge
     kernel), `launches` (0 by size, 1 one launch where the cut allows it, 2 two
     launches) or `wait_ticks` (bound of the one-launch wait, 100 MHz ticks; 0 is
     the default) the call goes through dspark_step_ex."""
+    args, out, ws = _step_args(hidden, w, bias, temps, tokens, logits, mode, cutoff, budget, out,
+                               ws, None)
+    if events is None and not launches and not wait_ticks:
+        _ok("dspark_step", lib().dspark_step(*args))
+    else:
+        ev = events if events is not None else (None, None)
+        _ok("dspark_step_ex", lib().dspark_step_ex(
+            *args, _event_handle(ev[0]), _event_handle(ev[1]), int(launches), int(wait_ticks)))
+    return out
+
+
+def _step_args(hidden, w, bias, temps, tokens, logits, mode, cutoff, budget, out, ws, stream):
+    """Checked, marshalled arguments of dspark_step (and the outputs)."""
     B, g, d = hidden.shape
     V = logits.shape[-1]
     _need(hidden, "hidden", torch.bfloat16)
@@ -407,19 +420,45 @@ def dspark_step(hidden, w, bias, temps, tokens, logits, mode, cutoff=None, budge
         if out.get(k) is not None:
             _need(out[k], k, torch.float32 if k in ("conf", "survival") else torch.int32, shp)
     ws = workspace(B, g, V, dev) if ws is None else _need(ws, "ws", torch.uint8)
+    st = _stream(dev) if stream is None else ctypes.c_void_p(int(stream))
     args = (
         _ptr(hidden), _ptr(w), float(bias), _ptr(temps), _ptr(tokens), _ptr(logits), B, g, d, V,
         m, _ptr(cutoff), int(budget), _ptr(out.get("conf")), _ptr(out.get("survival")),
         _ptr(out["lengths"]), _ptr(out["cu_seqlens"]), _ptr(out["packed_tokens"]),
         _ptr(out["packed_src_row"]), _ptr(out["packed_argmax"]), _ptr(out["accepted"]),
-        _ptr(out["bonus"]), _ptr(ws), ws.numel(), _stream(dev))
-    if events is None and not launches and not wait_ticks:
-        _ok("dspark_step", lib().dspark_step(*args))
-    else:
-        ev = events if events is not None else (None, None)
-        _ok("dspark_step_ex", lib().dspark_step_ex(
-            *args, _event_handle(ev[0]), _event_handle(ev[1]), int(launches), int(wait_ticks)))
-    return out
+        _ptr(out["bonus"]), _ptr(ws), ws.numel(), st)
+    return args, out, ws
+
+
+class BoundStep:
+    """dspark_step on fixed buffers: the arguments are checked and marshalled
+    once, and each call is one C call (for serving loops that refill the same
+    input buffers every step, where the per-call checks of dspark_step cost
+    more host time than a small step takes on the GPU). The tensors must stay
+    alive, in place and unresized while the object is used; calls run on the
+    stream given at binding (the current stream by default)."""
+
+    def __init__(self, hidden, w, bias, temps, tokens, logits, mode, cutoff=None, budget=0,
+                 out=None, ws=None, launches=0, wait_ticks=0, stream=None):
+        args, self.out, self.ws = _step_args(hidden, w, bias, temps, tokens, logits, mode, cutoff,
+                                             budget, out, ws, stream)
+        # the tensors the raw pointers point into
+        self._keep = (hidden, w, temps, tokens, logits, cutoff, self.out, self.ws)
+        self._fn = lib().dspark_step_ex
+        self._args = args + (None, None, int(launches), int(wait_ticks))
+
+    def __call__(self):
+        status = self._fn(*self._args)
+        if status != 0:
+            raise DsparkError("dspark_step_ex", status)
+        return self.out
+
+
+def bind_step(hidden, w, bias, temps, tokens, logits, mode, cutoff=None, budget=0, out=None,
+              ws=None, launches=0, wait_ticks=0, stream=None) -> BoundStep:
+    """A BoundStep: dspark_step's arguments checked once, launched by calling it."""
+    return BoundStep(hidden, w, bias, temps, tokens, logits, mode, cutoff=cutoff, budget=budget,
+                     out=out, ws=ws, launches=launches, wait_ticks=wait_ticks, stream=stream)
 
 
 def dspark_step_ex(hidden, w, bias, temps, tokens, logits, mode, cutoff=None, budget=0,
@@ -479,7 +518,7 @@ def dspark_step_status(ws=None, status=None, device=None):
 __all__ = ["DsparkError", "lib", "LIB_PATH", "dspark_status_string", "dspark_confidence", "dspark_schedule",
            "dspark_compact", "dspark_accept", "dspark_step", "dspark_cap_accept",
            "dspark_gather_rows", "dspark_tier_select", "dspark_cost_cutoff",
-           "dspark_step_ex", "dspark_step_status", "dspark_step_noalloc",
+           "dspark_step_ex", "dspark_step_status", "dspark_step_noalloc", "BoundStep", "bind_step",
            "dspark_workspace_bytes",
            "dspark_workspace_init", "workspace", "alloc_step_outputs", "STEP_OUTPUTS",
            "DSPARK_CUT_THRESHOLD", "DSPARK_CUT_BUDGET", "DSPARK_CUT_STATIC",
