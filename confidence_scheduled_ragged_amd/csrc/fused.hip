@@ -66,18 +66,21 @@ constexpr int kStreamUnroll = 2;  // 16-byte loads in flight per lane (more wave
 constexpr int kRootUnrollDeep = 4;
 // Smallest batch that takes the one-launch form by default. Below it the
 // in-grid wait for the lengths costs more than the second launch it saves
-// (measured at gamma = 16, d = 4096, V = 151936: two launches faster by about
-// 2 us at B = 1..32 and 1 us at B = 64, one launch faster by 2.4 us at
-// B = 128 and 3-5 us at B = 256).
+// (measured at gamma = 16, d = 4096, V = 151936 with back-to-back steps: two
+// launches 14.5 us against 15.2 at B = 1 and 24.7 against 25.1-27 at B = 64;
+// one launch faster by a few microseconds from B = 128 up).
 constexpr int kOneLaunchMinB = 96;
 // The one-launch step: 16-byte loads in flight per lane in the GEMV, the root
 // rows and the draft rows (its grid holds four waves per SIMD, so deeper
 // unrolling costs no occupancy), and the extra draft slots per early wave, as
 // a fraction of a root wave's root-row slots: about the root work left when
-// the lengths come out.
+// the lengths come out. Measured on the mixed workload's threshold arm: draft
+// rows four deep 104.7 us per step, two deep 106.2, six or eight deep
+// 107.7-109.5; root rows two or eight deep slower than four; a lead of 0.6 to
+// 0.8 alike.
 constexpr int kOneGemvUnroll = 4;
 constexpr int kOneRootUnroll = 4;
-constexpr int kOneStreamUnroll = 2;
+constexpr int kOneStreamUnroll = 4;
 // Short sub-chunks (at most kShortSub slots: small steps, where a wave's
 // sub-chunk is a chain of dependent load rounds rather than a share of the
 // bandwidth) are streamed with eight 16-byte loads in flight per lane, so
