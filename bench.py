@@ -639,6 +639,10 @@ def main():
                          "d=7168 V=129280 T=768; or the mixed workload's budget or combined "
                          "arm), for a kernel trace of it; prints its arm summary instead of the "
                          "JSON line")
+    ap.add_argument("--latency-only", action="store_true",
+                    help="time only the batch-1 and mid latency arm (eager, bound, one step per "
+                         "graph, several steps per graph), for a kernel trace of it; prints the "
+                         "arm's records instead of the JSON line")
     ap.add_argument("--no-all-cores", action="store_true",
                     help="skip the oracle timing on all host cores")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -665,6 +669,11 @@ def main():
         ws4 = dspark.workspace(cfg4.B, cfg4.gamma, cfg4.V, dev)
         r_4 = run_arm(cfg4, slots4, outs4, ws4, args.steps, args.warmup, dspark, torch)
         print(json.dumps(arm_summary(cfg4, r_4, args.steps, cfg4.B)), flush=True)
+        return
+    if args.latency_only:
+        lat = [run_graph_latency(CONFIGS[n], args.steps, dspark, torch, make_step, make_params)
+               for n in ("batch1", "mid")]
+        print(json.dumps(lat), flush=True)
         return
     cfg_t = CONFIGS["mixed_threshold"]
     cfg_b = CONFIGS["mixed_budget"]

@@ -280,7 +280,10 @@ dspark_status dspark_cap_accept(const int32_t *packed_argmax_full, const int32_t
  * call that gave up are undefined; later calls on the same workspace are not
  * affected (every call starts its counters afresh), so no re-initialisation is
  * needed. A give-up does not happen while the device runs nothing else that
- * holds its compute units for that long.
+ * holds its compute units for that long. In either form, the wave that
+ * finishes a request may re-read a key slot whose store, issued before the
+ * count that made that wave the finisher, has not landed yet; that re-read has
+ * the same bound and, should it give up, sets the same flag.
  */
 dspark_status dspark_step(const dspark_bf16 *hidden, const dspark_bf16 *w, float bias,
                           const float *temps, const int32_t *tokens, const dspark_bf16 *logits,
@@ -303,10 +306,11 @@ dspark_status dspark_step(const dspark_bf16 *hidden, const dspark_bf16 *w, float
  *     does), 1 asks for the one-launch form where the cut allows it (threshold
  *     and static cuts, grid resident at once), 2 for two launches;
  *     DSPARK_ERR_ARG for any other value.
- *   wait_ticks: bound of the one-launch form's wait for the lengths, in ticks
- *     of the device's 100 MHz constant clock; 0 means the default (about one
- *     second). A bound too short for the lengths makes workgroups give up, as
- *     described under dspark_step; tests use it to drive that path.
+ *   wait_ticks: bound of the one-launch form's wait for the lengths (and of a
+ *     finishing wave's re-read of a key slot), in ticks of the device's 100 MHz
+ *     constant clock; 0 means the default (about one second). A bound too
+ *     short for the lengths makes workgroups give up, as described under
+ *     dspark_step; tests use it to drive that path.
  */
 dspark_status dspark_step_ex(const dspark_bf16 *hidden, const dspark_bf16 *w, float bias,
                              const float *temps, const int32_t *tokens, const dspark_bf16 *logits,
@@ -321,7 +325,7 @@ dspark_status dspark_step_ex(const dspark_bf16 *hidden, const dspark_bf16 *w, fl
 /*
  * The fused step's give-up flag: enqueues on `stream` a read of the 32-bit word
  * at byte 192 of ws into status[0] (device int32: 0 when no workgroup of any
- * dspark_step / dspark_step_ex call since the last read gave up its bounded
+ * dspark_step / dspark_step_ex call since the last read gave up a bounded
  * wait, 1 otherwise) and clears the word, without synchronising. ws: the
  * workspace those calls used (16-byte aligned).
  */
