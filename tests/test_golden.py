@@ -3,9 +3,9 @@
 worked_verify_block.json is a verify step of two requests worked out by hand
 from the pages' definitions (head, survival, the three cuts, packing, greedy
 acceptance, bonus): the oracle must reproduce it (CPU), and so must the HIP
-library through the fused step in both forms (for batch-wide picks the
-one-launch form is step_pick_kernel) and through the stage entry points (GPU). oracle_small_case.json holds the oracle's outputs for one
-seeded step, written by tests/golden/make_oracle_case.py; the oracle must
+library through the fused step in both forms (batch-wide picks take two
+launches in either) and through the stage entry points (GPU).
+oracle_small_case.json holds the oracle's outputs for one seeded step, written by tests/golden/make_oracle_case.py; the oracle must
 still reproduce it bit for bit, and the HIP library must match it.
 """
 import json
