@@ -81,11 +81,15 @@ constexpr int kOneLaunchMinB = 96;
 constexpr int kOneGemvUnroll = 4;
 constexpr int kOneRootUnroll = 4;
 constexpr int kOneStreamUnroll = 4;
-// Short sub-chunks (at most kShortSub slots: small steps, where a wave's
-// sub-chunk is a chain of dependent load rounds rather than a share of the
-// bandwidth) are streamed with eight 16-byte loads in flight per lane, so
-// 16 KiB is two rounds instead of eight.
-constexpr int kStreamUnrollShort = 8;
+// Short sub-chunks (at most kShortSub slots) are streamed with four 16-byte
+// loads in flight per lane. Measured with back-to-back steps at B = 256
+// (sub-chunks of about 3400 slots): the budget arms take 66.9-67.0 us per step
+// (mixed traffic, T = 742) and 66.1 us (d = 7168) with four, against 68.3 and
+// 67.7 with eight, 67.5 and 65.9 with three, 68.4 and 66.8 with six; steps at
+// B = 1 and B = 64 take as long with four as with eight. Once the waves keep
+// the memory system full, more loads in flight per wave only lengthen every
+// round trip, the finishing waves' included.
+constexpr int kStreamUnrollShort = 4;
 constexpr int64_t kShortSub = 4096;
 // Minimum sub-chunk of the fused step's root and draft rows: 4 KiB of bf16, one
 // load round of a wave at four 16-byte loads per lane. Small steps then spread
@@ -625,7 +629,9 @@ __global__ __launch_bounds__(kStreamThreads) void step_stream_kernel(StreamParam
     const int64_t K = step_sub_len(E, p.target_waves);
     const int64_t Kr = step_sub_len((int64_t)B * Vv, p.root_waves);
     auto sub = [&](int64_t e) { return udiv64(e, K); };
-    // requests without draft rows are finished by the workgroup that owns them
+    // requests without draft rows are finished by the workgroup that owns
+    // them, after its first wave's stream (a finish started first would delay
+    // that wave's rows by its round trips)
     if (tid < kWave)
         for (int b = blockIdx.x; b < B; b += gridDim.x)
             if (len_s[b] == 0)
