@@ -55,6 +55,13 @@ constexpr int kFusedSelMax = kFusedSelPer * kFrontThreads;
 constexpr int kFrontRootWGsPerCU = 1;  // root-row workgroups of the front grid per CU
 constexpr int kStreamThreads = 512;
 constexpr int kStreamWavesPerCU = 16;  // target waves of the draft-row stream per CU
+// The same target for batches below kOneLaunchMinB requests: fewer waves, each
+// with a longer run.
+// Measured with back-to-back steps (gamma = 16, d = 4096, V = 151936): at B = 64
+// a step takes 24.1-24.3 us with 8 per CU, 24.4-24.5 with 12 and 25.5 with 16,
+// and at B = 1 as long with 8 as with 16; at B = 256 the budget arms are 3.4 us
+// slower with 12 per CU than with 16, and 12 us slower with 8.
+constexpr int kStreamWavesPerCUSmall = 8;
 constexpr int kStreamUnroll = 2;  // 16-byte loads in flight per lane (more waves, fewer bytes each)
 // Root rows of the front kernel: four 16-byte loads in flight per lane when
 // they are the front's critical path, two when the GEMV-and-pick chain is (the
@@ -1015,7 +1022,8 @@ hipError_t launch_fused_step(const uint16_t *hidden, const uint16_t *w, float bi
     p.keys = keys;
     p.rkeys = rkeys;
     p.arrivals = rcnt;
-    p.target_waves = kStreamWavesPerCU * cus < kMaxWaves ? kStreamWavesPerCU * cus : (int)kMaxWaves;
+    const int wpc = B < kOneLaunchMinB ? kStreamWavesPerCUSmall : kStreamWavesPerCU;
+    p.target_waves = wpc * cus < kMaxWaves ? wpc * cus : (int)kMaxWaves;
     p.root_waves = root_waves;
     p.timed_out = reinterpret_cast<unsigned *>(wsb + ws_ctrl_offset() + kCtrlTimedOutOffset);
     p.wait_ticks = wait_ticks ? wait_ticks : kWaitTicks;
