@@ -2,11 +2,12 @@
 cap-accept audit logs (host code, numpy only).
 
 [P1] "DFlash to DSpark in SGLang", section "DSpark: a sequential head and a
-verify budget": the head scores each drafted token's chance of surviving
-verification, the product over the block is its survival probability, and
-STS calibrates it against true acceptance rates; section "The confidence
-scheduler and verify modes": the cap-accept arm records what a full verify
-accepts. Those records are the labels this fit needs.
+verify budget": the head estimates, per drafted token, the probability that
+the target keeps it; multiplied along the block these give the survival
+probability, and STS tunes one temperature per position so the estimates
+match measured acceptance; section "The confidence scheduler and verify
+modes": the cap-accept arm logs, beside what it commits, the acceptance of the
+whole block. Those records are the labels this fit needs.
 
 Model (the same one the kernels apply): position i of a drafted block survives,
 given that every earlier draft survived, with probability sigma(z_i / T_i),

@@ -3,9 +3,10 @@
 // stage kernel and the fused step kernel.
 //
 // [P1] "DFlash to DSpark in SGLang", section "DSpark: a sequential head and a
-// verify budget": the head is a linear projection plus a sigmoid of the
-// drafter hidden state, calibrated per block position by a temperature, and
-// the survival curve is the running product of the per-position scores.
+// verify budget": each drafted position's score is one dot product of the
+// drafter's hidden state with a weight vector (plus a bias), divided by that
+// block position's temperature and squashed by the logistic function; the
+// survival curve multiplies the scores up to each position.
 #pragma once
 
 #include "common.hpp"

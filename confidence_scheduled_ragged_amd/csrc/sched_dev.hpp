@@ -2,8 +2,8 @@
 // and the block-wide scan used by compaction, as device functions.
 //
 // [P1] "DFlash to DSpark in SGLang": the per-request cut of section "The
-// confidence scheduler and verify modes" (stop walking the survival curve
-// where the gain no longer covers the marginal cost) and the batch-wide
+// confidence scheduler and verify modes" (a request's window grows while the
+// survival at the next position is worth its per-token cost) and the batch-wide
 // verify-length top-k schedule of section "Zero-overhead scheduling and
 // kernels"; [P2] contrasts the dynamic budget with a fixed one.
 #pragma once

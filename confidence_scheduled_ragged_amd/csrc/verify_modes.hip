@@ -4,7 +4,7 @@
 // [P1] "DFlash to DSpark in SGLang", section "The confidence scheduler and
 // verify modes": cap-accept pays the static verify but commits only the
 // scheduled window, so its committed output equals compact's exactly, and it
-// records what the full verify would have accepted; the ratio of the two sums
+// logs the acceptance of the whole block beside it; the ratio of the two sums
 // is the scheduler's utilisation.
 #include "common.hpp"
 

@@ -93,10 +93,11 @@ typedef enum dspark_cut_mode {
 
 /*
  * Steps 1-2 [P1, "DSpark: a sequential head and a verify budget"]: the
- * confidence head is a linear projection plus a sigmoid of each drafted
- * position's drafter hidden state, calibrated per position by Sequential
- * Temperature Scaling; the block's survival curve is the running product of
- * those scores.
+ * score of each drafted position is a dot product of its drafter hidden
+ * state with one weight vector plus a bias, divided by that position's
+ * Sequential Temperature Scaling temperature and passed through the logistic
+ * function; the block's survival curve multiplies those scores up to each
+ * position.
  *   conf[b,i]     = 1 / (1 + exp(-(sum_k w[k]*hidden[b,i,k] + bias) / temps[i]))
  *   survival[b,i] = conf[b,0] * ... * conf[b,i]   (S_{i+1}; S_0 = 1 implicit)
  * hidden [B, gamma, d] bf16; w [d] bf16; bias host fp32; temps [gamma] fp32 (> 0).
@@ -176,8 +177,8 @@ dspark_status dspark_tier_select(const int32_t *cu_seqlens, int B, int gamma,
 
 /*
  * Packed row gather [P1, "Ragged verify under full CUDA graphs"]: the
- * scheduled verify tokens are front-packed into one [total_tokens, hidden]
- * buffer, the layout the target's per-row matmuls already use. Gathers rows of
+ * scheduled verify rows sit back to back, with no padding, in a single
+ * buffer of total-tokens rows, which suits the target's row-wise matmuls. Gathers rows of
  * any width through the packed source rows of dspark_compact:
  *   dst[r, :] = src[packed_src_row[r], :]   for r < cu_seqlens[B]
  * src: B*(gamma+1) rows of row_bytes bytes (e.g. per-position activations
@@ -235,7 +236,7 @@ dspark_status dspark_accept(const dspark_bf16 *logits, const int32_t *packed_src
  * Steps 5b-6 in the cap-accept verify mode [P1, "The confidence scheduler and
  * verify modes"]: the audit arm pays the full (static) verify but commits only
  * the scheduled window, so its committed output equals the compact mode's
- * exactly while it records what a full verify would have accepted.
+ * exactly while it logs the acceptance of the whole block beside it.
  *   packed_argmax_full [B*(gamma+1)] int32: the target's choice at every row
  *     of the full block, static packing (request b's row j at b*(gamma+1)+j),
  *     e.g. the packed_argmax of dspark_step in DSPARK_CUT_STATIC mode;

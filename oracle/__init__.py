@@ -160,8 +160,8 @@ def cap_accept(lengths, tokens, amax_full):
 
 
 def utilization(accepted, accepted_full):
-    """The audit metric: tokens committed under the window over tokens a full
-    verify would have accepted (1.0 when nothing would have been accepted)."""
+    """The audit metric: tokens committed under the window over the tokens that
+    verifying the whole block accepts (1.0 when that is none)."""
     a = int(np.sum(np.asarray(accepted, np.int64)))
     f = int(np.sum(np.asarray(accepted_full, np.int64)))
     return 1.0 if f == 0 else a / f

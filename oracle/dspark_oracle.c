@@ -115,9 +115,9 @@ int oracle_survival(const double *conf, int B, int gamma, double *surv)
 
 /*
  * Step 3, per-request cut [P1, "DSpark: a sequential head and a verify
- * budget" and "The confidence scheduler and verify modes"]: walk down the
- * survival curve and stop where the expected gain of one more verify token no
- * longer covers its marginal cost c_b. Verifying draft k gains S_k expected
+ * budget" and "The confidence scheduler and verify modes"]: the window
+ * extends one position at a time along the survival curve for as long as the
+ * tokens the next position is expected to add pay for its per-token cost c_b. Verifying draft k gains S_k expected
  * tokens, so draft k is kept while S_k >= c_b (reading: ">=" keeps a tie).
  * The verify length is the number of kept drafts,
  *     L_b = #{k in 1..gamma : S_k >= c_b},
@@ -251,9 +251,9 @@ int oracle_cut_combined(const double *surv, const float *cutoff, int B, int gamm
 
 /*
  * Cost-table cutoff [P1, "The confidence scheduler and verify modes"]: the
- * server measures how much each extra verify token adds to the step time at
- * each load and stores it as a cost table; higher load raises the marginal
- * cost and tightens every window together. Reading: table[j] is the marginal
+ * server times the step cost of one more verify token at each load level
+ * and keeps those figures as a cost table; under a heavier load each token
+ * costs more, so all windows shrink at once. Reading: table[j] is the marginal
  * cost at load level j already expressed in expected tokens (the unit of the
  * survival values), and every request of the step gets the entry of the
  * step's load level, clamped to the table:
@@ -272,7 +272,7 @@ int oracle_cost_cutoff(const float *table, int n, int32_t load, int B, float *cu
 /*
  * Step 4, ragged compaction [P1, "Ragged verify under full CUDA graphs"]: the
  * scheduled verify rows of all requests are front-packed with no padding, and
- * a cu_seqlens array marks where each request's segment starts. Request b
+ * cu_seqlens gives the first packed row of each request (and the total last). Request b
  * verifies L_b + 1 rows: its root row j = 0 plus drafts 1..L_b. With the dense
  * verify block laid out as [B, gamma+1] (column 0 = root token),
  *     cu[0] = 0,  cu[b+1] = cu[b] + L_b + 1,
@@ -308,8 +308,8 @@ int oracle_compact(const int32_t *lengths, const int32_t *tokens, int B, int gam
 
 /*
  * Packed row gather [P1, "Ragged verify under full CUDA graphs"]: the
- * scheduled verify tokens' per-row data is front-packed into one
- * [total_tokens, hidden] buffer. Row r < cu[B] of dst is a byte copy of row
+ * per-row data of the scheduled verify tokens sits back to back, with no
+ * padding, in a buffer of total-tokens rows. Row r < cu[B] of dst is a byte copy of row
  * packed_src_row[r] of src (rows of row_bytes bytes); later rows are left as
  * they are. A source row outside [0, B*(gamma+1)) is rejected.
  */
@@ -335,8 +335,8 @@ int oracle_gather_rows(const uint8_t *src, const int32_t *packed_src_row,
 
 /*
  * Graph tier of a packed batch [P1, "Ragged verify under full CUDA graphs"]:
- * the verify graph is keyed on the packed total rounded up to the nearest
- * captured tier, and the packed batch is padded up to that tier.
+ * a batch runs the captured verify graph of the smallest tier that holds its
+ * packed total, with its packed rows padded out to that tier's size.
  *   tier_index = smallest t with tiers[t] >= total (tiers ascending), or
  *                ntiers when no captured tier holds the batch;
  *   padded     = tiers[tier_index], or total when there is no such tier.
@@ -440,7 +440,7 @@ int oracle_accept(const int32_t *cu_seqlens, const int32_t *tokens, const int32_
 /*
  * Step 3 in the static verify mode [P1, "The confidence scheduler and verify
  * modes"]: the full drafted block is verified, L_b = gamma for every request.
- * It is the no-trim baseline.
+ * Nothing is cut, so it is the reference the other modes are measured against.
  */
 int oracle_cut_static(int B, int gamma, int32_t *lengths)
 {

@@ -2,9 +2,9 @@
 cost-table cutoff (needs an MI355X).
 
 [P1] "DFlash to DSpark in SGLang", section "The confidence scheduler and
-verify modes": each request's window stops where its gain no longer covers the
-marginal cost, the cost comes from a table measured per load, and higher load
-tightens every window; section "Zero-overhead scheduling and kernels": the
+verify modes": a request's window ends at the first position whose survival is
+below the per-token cost, that cost is read from a table timed per load level,
+and a heavier load shrinks all windows at once; section "Zero-overhead scheduling and kernels": the
 batch-wide verify-length top-k schedule. The oracle computes its own cutoffs,
 cuts and steps from the generated inputs only.
 """

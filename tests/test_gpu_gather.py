@@ -1,8 +1,8 @@
 """GPU parity of the packed row gather (needs an MI355X).
 
 [P1] "DFlash to DSpark in SGLang", section "Ragged verify under full CUDA
-graphs": the scheduled verify tokens are front-packed into one
-[total_tokens, hidden] buffer. dspark_gather_rows moves per-position rows of
+graphs": the per-row data of the scheduled verify tokens sits back to back,
+with no padding, in a buffer of total-tokens rows. dspark_gather_rows moves per-position rows of
 any width through the packed source rows of the compaction; the result must
 be a byte-exact copy of the oracle's gather, with every row past the packed
 total left untouched.

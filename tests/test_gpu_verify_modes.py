@@ -3,7 +3,7 @@
 [P1] "DFlash to DSpark in SGLang", section "The confidence scheduler and
 verify modes": static verifies the full block; cap-accept pays that verify but
 commits only the cut's window, so its committed output equals compact's
-exactly, and it records what the full verify would have accepted.
+exactly, and it logs the acceptance of the whole block beside it.
 
 The oracle sees only generated inputs: it computes its own full-block argmax,
 its own cut and its own cap. The GPU's cap-accept result is compared with the
