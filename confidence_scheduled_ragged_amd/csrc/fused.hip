@@ -56,11 +56,16 @@ constexpr int kFrontRootWGsPerCU = 1;  // root-row workgroups of the front grid 
 constexpr int kStreamThreads = 512;
 constexpr int kStreamWavesPerCU = 16;  // target waves of the draft-row stream per CU
 // The same target for batches below kOneLaunchMinB requests: fewer waves, each
-// with a longer run.
-// Measured with back-to-back steps (gamma = 16, d = 4096, V = 151936): at B = 64
-// a step takes 24.1-24.3 us with 8 per CU, 24.4-24.5 with 12 and 25.5 with 16,
-// and at B = 1 as long with 8 as with 16; at B = 256 the budget arms are 3.4 us
-// slower with 12 per CU than with 16, and 12 us slower with 8.
+// with a longer run, and every sub-chunk kStreamUnrollShort loads deep whatever
+// its length (half the waves need the deeper pipelines to keep as many bytes in
+// flight). Measured with back-to-back two-launch steps (gamma = 16, d = 4096,
+// V = 151936, mixed traffic with cutoff 0.25 unless stated), against 16 waves
+// per CU: B = 32 26.3 us against 27.9; B = 64 37.9 against 39.0; B = 95 50.0
+// against 51.6; B = 64 static 61.2 against 63.5; B = 64 with cutoffs in
+// [0.1, 0.5] 22.6 against 24.8; B = 64 under a budget of 2.9 per request 30.9
+// against 31.7. Six or eight loads deep: 0.3-1.2 us slower. At B = 256 the
+// budget arms are 3.4 us slower with 12 waves per CU than with 16, and 12 us
+// slower with 8.
 constexpr int kStreamWavesPerCUSmall = 8;
 constexpr int kStreamUnroll = 2;  // 16-byte loads in flight per lane (more waves, fewer bytes each)
 // Root rows of the front kernel: four 16-byte loads in flight per lane when
@@ -340,6 +345,7 @@ struct StreamParams {
     uint64_t *arrivals;     // [B] streamed slots per request (zero between calls)
     int target_waves;       // sub-chunk length: about one sub-chunk per target wave
     int root_waves;         // waves that streamed the root rows
+    int deep;               // 1: every draft sub-chunk kStreamUnrollShort loads deep
     unsigned *timed_out;    // sticky: set when a wait for a key gave up
     unsigned long long wait_ticks;  // bound of such a wait, in 100 MHz clock ticks
 };
@@ -610,7 +616,7 @@ __device__ __forceinline__ void stream_draft_rows(const StreamParams &p, const i
     const int64_t NS = udiv64(E + K - 1, K);
     for (int64_t cur = w; cur < NS; cur += W) {
         const int64_t e0 = cur * K, e1 = cur * K + K < E ? cur * K + K : E;
-        if (K <= kShortSub)
+        if (K <= kShortSub || p.deep)
             stream_draft_span<kVec, kStreamUnrollShort, true, false>(p, cu_s, Vv, Kr, cur, e0, e1,
                                                                      arrive);
         else
@@ -1025,6 +1031,7 @@ hipError_t launch_fused_step(const uint16_t *hidden, const uint16_t *w, float bi
     const int wpc = B < kOneLaunchMinB ? kStreamWavesPerCUSmall : kStreamWavesPerCU;
     p.target_waves = wpc * cus < kMaxWaves ? wpc * cus : (int)kMaxWaves;
     p.root_waves = root_waves;
+    p.deep = B < kOneLaunchMinB ? 1 : 0;
     p.timed_out = reinterpret_cast<unsigned *>(wsb + ws_ctrl_offset() + kCtrlTimedOutOffset);
     p.wait_ticks = wait_ticks ? wait_ticks : kWaitTicks;
     // draft segment keys in use: keys[s + r] with s below the sub-chunk count

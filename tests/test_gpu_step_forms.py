@@ -68,6 +68,10 @@ CASES = {
     # the largest batch of the fused step: each request workgroup runs 16
     # requests, and cu_seqlens fills 32 KiB of LDS
     "max_batch": CONFIGS["tiny"].scaled(B=4096, gamma=4, d=128, V=512),
+    # below 96 requests the two-launch stream runs half the waves, each
+    # sub-chunk (here over 4096 slots) four loads deep
+    "small_batch_long": CONFIGS["mixed_threshold"].scaled(B=95),
+    "small_batch_static": CONFIGS["mixed_threshold"].scaled(B=64, mode="static"),
     # batch-wide picks (two launches under either setting): B*gamma = 4096
     # positions, the most the in-kernel pick takes; d = 7168 stages a 14 KiB
     # head; odd d and V take the scalar paths; a batch over 4096 positions
