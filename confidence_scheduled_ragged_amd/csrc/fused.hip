@@ -49,7 +49,6 @@
 namespace dspark {
 
 constexpr int kFrontThreads = 512;
-constexpr int kFrontMaxLdsW = 16384;
 constexpr int kFusedSelPer = 8;  // survival values per thread of the in-front select
 constexpr int kFusedSelMax = kFusedSelPer * kFrontThreads;
 constexpr int kFrontRootWGsPerCU = 1;  // root-row workgroups of the front grid per CU
@@ -286,7 +285,11 @@ __device__ __forceinline__ void front_pick(const FrontParams &p, float *sv, uint
     budget_lengths(sv, nullptr, p.B, p.gamma, cut, p.lengths, scan_lds);
 }
 
-template <bool kVecH, bool kLdsW, bool kVecV, int kRootUnroll, int kGemvU = kGemvUnroll>
+// Request workgroups read the head w from global memory (L2): staging it in LDS
+// first, one more round trip before the GEMV, measured 0.7 us slower on the
+// budget arm of the mixed traffic workload (B = 256, d = 4096) and no faster
+// at d = 7168.
+template <bool kVecH, bool kVecV, int kRootUnroll, int kGemvU = kGemvUnroll>
 __global__ __launch_bounds__(kFrontThreads) void step_front_kernel(FrontParams p) {
     extern __shared__ __align__(16) uint16_t dyn_lds[];
     __shared__ float z_s[DSPARK_MAX_GAMMA], p_s[DSPARK_MAX_GAMMA], s_s[DSPARK_MAX_GAMMA];
@@ -306,15 +309,9 @@ __global__ __launch_bounds__(kFrontThreads) void step_front_kernel(FrontParams p
         __hip_atomic_store(req_counter(p.req_arrivals, b), (uint64_t)0, __ATOMIC_RELAXED,
                            __HIP_MEMORY_SCOPE_AGENT);
     zero_key_part(p, b, p.B);
-    const uint16_t *wp = p.w;
-    if (kLdsW) {
-        stage_w(p.w, p.d, dyn_lds);
-        __syncthreads();
-        wp = dyn_lds;
-    }
     // the select reads survival from another workgroup of this grid
     const bool select_here = p.arrivals != nullptr;
-    front_request<kVecH, kGemvU>(p, wp, b, select_here, false, z_s, p_s, s_s);
+    front_request<kVecH, kGemvU>(p, p.w, b, select_here, false, z_s, p_s, s_s);
     if (!select_here) return;
 
     // budget: count this request as done once its survival stores are complete;
@@ -329,7 +326,7 @@ __global__ __launch_bounds__(kFrontThreads) void step_front_kernel(FrontParams p
     __syncthreads();
     if (!last_s) return;
     if (tid == 0) __hip_atomic_store(p.arrivals, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    front_pick(p, reinterpret_cast<float *>(dyn_lds), hist, sh, scan_lds);  // w is no longer needed
+    front_pick(p, reinterpret_cast<float *>(dyn_lds), hist, sh, scan_lds);
 }
 
 // ----------------------------------------------------------------- stream
@@ -879,39 +876,34 @@ static int stream_grid(size_t lds) {
     return gsz;
 }
 
-// Front grids of at most one workgroup per CU (small batches) take the head
-// from global memory (no staging round trip) and eight 16-byte hidden loads in
-// flight per lane: a request's GEMV is then one load round per wave. Their
+// Front grids of at most one workgroup per CU (small batches) take eight
+// 16-byte hidden loads in flight per lane: a request's GEMV is then one load
+// round per wave. Their
 // occupancy (three waves per SIMD) still holds one workgroup per CU.
 constexpr int kGemvUnrollSmall = 8;
 
 template <bool kVecV, int kRootUnroll>
-static void launch_front_u(bool hvec, bool ldsw, const FrontParams &fp, int root_wgs, size_t lds,
+static void launch_front_u(bool hvec, const FrontParams &fp, int root_wgs, size_t lds,
                            hipStream_t s) {
     const dim3 grid(fp.B + root_wgs), block(kFrontThreads);
     if (hvec && fp.B + root_wgs <= device_cu_count())
-        hipLaunchKernelGGL((step_front_kernel<true, false, kVecV, kRootUnroll, kGemvUnrollSmall>),
-                           grid, block, lds, s, fp);
-    else if (hvec && ldsw)
-        hipLaunchKernelGGL((step_front_kernel<true, true, kVecV, kRootUnroll>), grid, block, lds, s,
-                           fp);
+        hipLaunchKernelGGL((step_front_kernel<true, kVecV, kRootUnroll, kGemvUnrollSmall>), grid,
+                           block, lds, s, fp);
     else if (hvec)
-        hipLaunchKernelGGL((step_front_kernel<true, false, kVecV, kRootUnroll>), grid, block, lds,
-                           s, fp);
+        hipLaunchKernelGGL((step_front_kernel<true, kVecV, kRootUnroll>), grid, block, lds, s, fp);
     else
-        hipLaunchKernelGGL((step_front_kernel<false, false, kVecV, kRootUnroll>), grid, block, lds,
-                           s, fp);
+        hipLaunchKernelGGL((step_front_kernel<false, kVecV, kRootUnroll>), grid, block, lds, s, fp);
 }
 
 template <bool kVecV>
-static void launch_front(bool hvec, bool ldsw, const FrontParams &fp, int root_wgs, size_t lds,
+static void launch_front(bool hvec, const FrontParams &fp, int root_wgs, size_t lds,
                          hipStream_t s) {
     const bool gemv_critical =
         fp.arrivals != nullptr && (int64_t)fp.gamma * fp.d * 2 > (int64_t)fp.V;
     if (gemv_critical)
-        launch_front_u<kVecV, kRootUnrollShallow>(hvec, ldsw, fp, root_wgs, lds, s);
+        launch_front_u<kVecV, kRootUnrollShallow>(hvec, fp, root_wgs, lds, s);
     else
-        launch_front_u<kVecV, kRootUnrollDeep>(hvec, ldsw, fp, root_wgs, lds, s);
+        launch_front_u<kVecV, kRootUnrollDeep>(hvec, fp, root_wgs, lds, s);
 }
 
 template <bool kVecH, bool kVecV>
@@ -970,7 +962,6 @@ hipError_t launch_fused_step(const uint16_t *hidden, const uint16_t *w, float bi
 
     const int N = B * gamma;
     const bool hvec = (d % 8 == 0) && (((uintptr_t)hidden | (uintptr_t)w) % 16 == 0);
-    const bool ldsw = hvec && d <= kFrontMaxLdsW;
     const bool select_in_front =
         (mode == DSPARK_CUT_BUDGET || mode == DSPARK_CUT_COMBINED) && N <= kFusedSelMax;
     const bool vvec = (V % 8 == 0) && ((uintptr_t)logits % 16 == 0);
@@ -994,8 +985,7 @@ hipError_t launch_fused_step(const uint16_t *hidden, const uint16_t *w, float bi
     fp.keys = keys;
     fp.req_arrivals = rcnt;
     fp.arrivals = select_in_front ? arrivals : nullptr;
-    size_t front_lds = ldsw ? (size_t)d * 2 : 0;
-    if (select_in_front && (size_t)N * 4 > front_lds) front_lds = (size_t)N * 4;
+    const size_t front_lds = select_in_front ? (size_t)N * 4 : 0;  // the pick's survival values
     // root-row workgroups: a fixed share of the chip, but no more than the
     // root rows fill with minimum-length sub-chunks
     const int cus = device_cu_count();
@@ -1081,9 +1071,9 @@ hipError_t launch_fused_step(const uint16_t *hidden, const uint16_t *w, float bi
     }
 
     if (vvec)
-        launch_front<true>(hvec, ldsw, fp, (int)root_wgs, front_lds, s);
+        launch_front<true>(hvec, fp, (int)root_wgs, front_lds, s);
     else
-        launch_front<false>(hvec, ldsw, fp, (int)root_wgs, front_lds, s);
+        launch_front<false>(hvec, fp, (int)root_wgs, front_lds, s);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
 

@@ -73,7 +73,7 @@ CASES = {
     "small_batch_long": CONFIGS["mixed_threshold"].scaled(B=95),
     "small_batch_static": CONFIGS["mixed_threshold"].scaled(B=64, mode="static"),
     # batch-wide picks (two launches under either setting): B*gamma = 4096
-    # positions, the most the in-kernel pick takes; d = 7168 stages a 14 KiB
+    # positions, the most the in-kernel pick takes; d = 7168 reads a 14 KiB
     # head; odd d and V take the scalar paths; a batch over 4096 positions
     # takes the stage kernel's pick
     "mixed_budget": CONFIGS["mixed_budget"].scaled(V=32768),
