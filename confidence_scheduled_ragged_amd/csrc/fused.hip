@@ -78,8 +78,10 @@ constexpr int kRootUnrollDeep = 4;
 // Smallest batch that takes the one-launch form by default. Below it the
 // in-grid wait for the lengths costs more than the second launch it saves
 // (measured at gamma = 16, d = 4096, V = 151936 with back-to-back steps: two
-// launches 14.5 us against 15.2 at B = 1 and 24.7 against 25.1-27 at B = 64;
-// one launch faster by a few microseconds from B = 128 up).
+// launches 14.5 us against 15.2 at B = 1 and 22.6-23.0 against 25.1-27 at
+// B = 64 with cutoffs in [0.1, 0.5]; at the boundary, with cutoff 0.25, two
+// launches at B = 95 take 50.0 us and one launch at B = 96 49.9 us; one launch
+// faster by a few microseconds from B = 128 up).
 constexpr int kOneLaunchMinB = 96;
 // The one-launch step: 16-byte loads in flight per lane in the GEMV, the root
 // rows and the draft rows (its grid holds four waves per SIMD, so deeper
@@ -639,9 +641,9 @@ __global__ __launch_bounds__(kStreamThreads) void step_stream_kernel(StreamParam
     const int64_t K = step_sub_len(E, p.target_waves);
     const int64_t Kr = step_sub_len((int64_t)B * Vv, p.root_waves);
     auto sub = [&](int64_t e) { return udiv64(e, K); };
-    // requests without draft rows are finished by the workgroup that owns
-    // them, after its first wave's stream (a finish started first would delay
-    // that wave's rows by its round trips)
+    // requests without draft rows are finished first, by the first wave of the
+    // workgroup that owns them (finishing them after that wave's stream
+    // measured no faster)
     if (tid < kWave)
         for (int b = blockIdx.x; b < B; b += gridDim.x)
             if (len_s[b] == 0)
