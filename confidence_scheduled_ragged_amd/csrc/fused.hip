@@ -68,12 +68,14 @@ constexpr int kStreamWavesPerCU = 16;  // target waves of the draft-row stream p
 constexpr int kStreamWavesPerCUSmall = 8;
 constexpr int kStreamUnroll = 2;  // 16-byte loads in flight per lane (more waves, fewer bytes each)
 // Root rows of the front kernel: four 16-byte loads in flight per lane when
-// they are the front's critical path, two when the GEMV-and-pick chain is (the
+// they are the front's critical path, three when the GEMV-and-pick chain is (the
 // last request workgroup runs the batch-wide pick after the slowest GEMV; a
 // request's GEMV reads gamma*d bf16, its root row V). Measured per step: the
 // mixed workload's threshold arm 111 us with four against 113-115 with two;
-// its budget arm (gamma*d = 65536 < V/2) 68.1 against 70.3; the budget
-// workload at d = 7168 (gamma*d = 114688 > V/2) 67.7 with two against 69.3.
+// its budget arm (gamma*d = 65536 < V/2) 68.1 against 70.3, and 66.1-67.0
+// with six or eight against 65.4-65.6 with four; the budget workload at
+// d = 7168 (gamma*d = 114688 > V/2) 64.7 with three against 65.2-65.4 with
+// two and 65.5 with four.
 constexpr int kRootUnrollDeep = 4;
 // Smallest batch that takes the one-launch form by default. Below it the
 // in-grid wait for the lengths costs more than the second launch it saves
@@ -115,7 +117,7 @@ __device__ __forceinline__ int64_t step_sub_len(int64_t E, int64_t Wt) {
     return k < kStepSubMin ? kStepSubMin : k;
 }
 constexpr double kLead = 0.70;
-constexpr int kRootUnrollShallow = 2;
+constexpr int kRootUnrollShallow = 3;
 
 // ------------------------------------------------------------------ front
 
