@@ -1,6 +1,7 @@
 // fused.hip - the whole verify step on one stream, in one launch (threshold
-// and static cuts) or two (budget and combined cuts, whose batch-wide pick
-// must see every request's survival).
+// and static cuts from kOneLaunchMinB requests up) or two (budget and combined
+// cuts, whose batch-wide pick must see every request's survival, and smaller
+// batches).
 //
 // One launch: a grid of request workgroups (the confidence GEMV of their
 // requests' gamma hidden rows, the STS sigmoid, the sequential survival
@@ -28,8 +29,10 @@
 //           wave that completes a request's draft rows finishes it as above.
 //
 // Long contiguous runs per wave were measured faster than small interleaved
-// sub-chunks (HBM row-buffer locality), and two 16-byte loads in flight per
-// lane with full occupancy faster than deeper unrolling with fewer waves.
+// sub-chunks (HBM row-buffer locality). Each stream keeps as many bytes in
+// flight as fill the memory system and no more (two to four 16-byte loads per
+// lane at full occupancy, by stream; deeper pipelines only lengthen every
+// round trip).
 // Dynamic hand-out through per-XCD atomic work queues was measured slower:
 // one queue address serves about one ticket per 11-15 ns. Grid-wide barriers
 // were measured at 16-76 us each and are not used; the one-launch form's
@@ -882,8 +885,8 @@ static int stream_grid(size_t lds) {
 
 // Front grids of at most one workgroup per CU (small batches) take eight
 // 16-byte hidden loads in flight per lane: a request's GEMV is then one load
-// round per wave. Their
-// occupancy (three waves per SIMD) still holds one workgroup per CU.
+// round per wave. Their occupancy (three waves per SIMD) still holds one
+// workgroup per CU.
 constexpr int kGemvUnrollSmall = 8;
 
 template <bool kVecV, int kRootUnroll>
