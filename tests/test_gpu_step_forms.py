@@ -72,6 +72,9 @@ CASES = {
     # sub-chunk (here over 4096 slots) four loads deep
     "small_batch_long": CONFIGS["mixed_threshold"].scaled(B=95),
     "small_batch_static": CONFIGS["mixed_threshold"].scaled(B=64, mode="static"),
+    # the full static block at full size: in two launches every sub-chunk is
+    # long (about 19 000 slots), two loads deep
+    "static_full": CONFIGS["mixed_threshold"].scaled(mode="static"),
     # batch-wide picks (two launches under either setting): B*gamma = 4096
     # positions, the most the in-kernel pick takes; d = 7168 reads a 14 KiB
     # head; odd d and V take the scalar paths; a batch over 4096 positions
