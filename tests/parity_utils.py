@@ -115,6 +115,12 @@ def oracle_front(h: HostStep) -> Front:
         c = h.cutoff.astype(np.float64)[:, None]
         amb = np.abs(surv - c) <= BAND
         lo, hi = _above(surv, c)
+    elif h.cfg.mode == "combined" and h.budget <= 0:
+        # a budget of zero keeps no position, whatever passes its cutoff
+        L = oracle.cut_combined(surv, h.cutoff, h.budget)
+        cap = 0
+        amb = np.zeros_like(surv, dtype=bool)
+        lo = hi = L
     elif h.cfg.mode == "combined":
         L = oracle.cut_combined(surv, h.cutoff, h.budget)
         c = h.cutoff.astype(np.float64)[:, None]

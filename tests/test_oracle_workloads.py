@@ -51,3 +51,25 @@ def test_planted_rows_have_unique_argmax():
         row = f[b, i]
         t = tok[b, i + 1]
         assert row[t] == row.max() and np.sum(row == row.max()) == 1
+
+
+def test_combined_band_with_zero_budget():
+    # With T = 0 the combined cut keeps nothing, so a position lying on its
+    # request's cutoff is not ambiguous: the parity bookkeeping must give every
+    # request the exact length 0 (it once took the cutoff's band instead, whose
+    # lower end counts the positions certainly above the cutoff).
+    import oracle
+    from parity_utils import oracle_front, snapshot
+
+    cfg = CONFIGS["tiny"].scaled(mode="combined", budget_per_request=0.0)
+    h = snapshot(make_step(cfg, 0))
+    _, conf = oracle.confidence(h.hidden, h.w, h.bias, h.temps)
+    surv = oracle.survival(conf)
+    # every request's second position on its cutoff, its first well above it
+    h.cutoff = surv[:, 1].astype(np.float32)
+    assert np.all(surv[:, 0] > surv[:, 1] + 1e-3)
+    f = oracle_front(h)
+    assert h.budget == 0
+    assert not f.lengths.any()
+    assert f.ambiguous_positions == 0
+    assert np.array_equal(f.len_lo, f.lengths) and np.array_equal(f.len_hi, f.lengths)
