@@ -56,6 +56,13 @@ constexpr int kFusedSelPer = 8;  // survival values per thread of the in-front s
 constexpr int kFusedSelMax = kFusedSelPer * kFrontThreads;
 constexpr int kFrontRootWGsPerCU = 1;  // root-row workgroups of the front grid per CU
 constexpr int kStreamThreads = 512;
+// Stream workgroups of 1024 threads from kOneLaunchMinB requests up (there the
+// two-launch form serves batch-wide picks): half as many workgroups scan the
+// lengths and write the schedule. Measured with back-to-back steps at B = 256:
+// the d = 7168 budget workload 64.4 us per step against 64.9 with 512 (mixed
+// traffic's budget and combined arms alike); below kOneLaunchMinB requests 512
+// stay (B = 64: 25.4-25.5 us with 1024 against 23.0).
+constexpr int kStreamThreadsLarge = 1024;
 constexpr int kStreamWavesPerCU = 16;  // target waves of the draft-row stream per CU
 // The same target for batches below kOneLaunchMinB requests: fewer waves, each
 // with a longer run, and every sub-chunk kStreamUnrollShort loads deep whatever
@@ -629,8 +636,8 @@ __device__ __forceinline__ void stream_draft_rows(const StreamParams &p, const i
     }
 }
 
-template <bool kVec>
-__global__ __launch_bounds__(kStreamThreads) void step_stream_kernel(StreamParams p) {
+template <bool kVec, int kThreads>
+__global__ __launch_bounds__(kThreads) void step_stream_kernel(StreamParams p) {
     extern __shared__ int smem[];
     int *len_s = smem;          // [B]
     int *cu_s = smem + p.B;     // [B + 1]
@@ -862,10 +869,10 @@ __global__ __launch_bounds__(kFrontThreads) void step_one_kernel(OneParams q) {
 
 // ----------------------------------------------------------------- launch
 
-template <bool kVec>
+template <bool kVec, int kThreads>
 static int stream_grid(size_t lds) {
     // resident workgroups of the stream kernel for this LDS size, cached per
-    // device and 4 KiB LDS bucket
+    // device and 4 KiB LDS bucket (per instantiation)
     static std::atomic<int> cache[64][13];
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
@@ -873,8 +880,8 @@ static int stream_grid(size_t lds) {
     int gsz = cache[dev][bucket].load(std::memory_order_relaxed);
     if (gsz > 0) return gsz;
     int blocks = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, step_stream_kernel<kVec>,
-                                                     kStreamThreads, (size_t)bucket * 4096) !=
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, step_stream_kernel<kVec, kThreads>,
+                                                     kThreads, (size_t)bucket * 4096) !=
             hipSuccess ||
         blocks < 1)
         blocks = 1;
@@ -1034,13 +1041,18 @@ hipError_t launch_fused_step(const uint16_t *hidden, const uint16_t *w, float bi
     // draft segment keys in use: keys[s + r] with s below the sub-chunk count
     // (at most the target waves) and r below the draft rows (B * gamma)
     fp.key_words = (int64_t)p.target_waves + (int64_t)B * gamma;
-    // stream workgroups: enough for the target waves, and no more than the
-    // largest possible draft rows (every request at gamma) fill with
-    // minimum-length sub-chunks
-    int stream_wgs_needed = (p.target_waves + kStreamThreads / kWave - 1) / (kStreamThreads / kWave);
+    // stream workgroups (of `threads`; 512-thread workgroups for the one-launch
+    // grid): enough for the target waves, and no more than the largest possible
+    // draft rows (every request at gamma) fill with minimum-length sub-chunks
     const int64_t max_sub = ((int64_t)B * gamma * Vv + kStepSubMin - 1) / kStepSubMin;
-    const int64_t max_wgs = (max_sub + kStreamThreads / kWave - 1) / (kStreamThreads / kWave);
-    if (max_wgs < stream_wgs_needed) stream_wgs_needed = max_wgs < 1 ? 1 : (int)max_wgs;
+    auto wgs_needed = [&](int threads) {
+        const int wpw = threads / kWave;
+        int n = (p.target_waves + wpw - 1) / wpw;
+        const int64_t max_wgs = (max_sub + wpw - 1) / wpw;
+        if (max_wgs < n) n = max_wgs < 1 ? 1 : (int)max_wgs;
+        return n;
+    };
+    const int stream_wgs_needed = wgs_needed(kFrontThreads);
 
     // one launch (threshold and static cuts, batches from kOneLaunchMinB):
     // request workgroups (one per CU at most, each looping over its requests),
@@ -1090,14 +1102,27 @@ hipError_t launch_fused_step(const uint16_t *hidden, const uint16_t *w, float bi
     }
 
     const size_t lds = (size_t)(2 * B + 1) * sizeof(int);
-    int g = vvec ? stream_grid<true>(lds) : stream_grid<false>(lds);
-    g = g < stream_wgs_needed ? g : stream_wgs_needed;
+    const bool large = B >= kOneLaunchMinB;
+    int g = large ? (vvec ? stream_grid<true, kStreamThreadsLarge>(lds)
+                          : stream_grid<false, kStreamThreadsLarge>(lds))
+                  : (vvec ? stream_grid<true, kStreamThreads>(lds)
+                          : stream_grid<false, kStreamThreads>(lds));
+    const int g_need = wgs_needed(large ? kStreamThreadsLarge : kStreamThreads);
+    g = g < g_need ? g : g_need;
     // measurement events bracket the dominant kernel (the draft-row stream)
     if (ev_start && (e = hipEventRecord(ev_start, s)) != hipSuccess) return e;
-    if (vvec)
-        hipLaunchKernelGGL((step_stream_kernel<true>), dim3(g), dim3(kStreamThreads), lds, s, p);
+    if (large && vvec)
+        hipLaunchKernelGGL((step_stream_kernel<true, kStreamThreadsLarge>), dim3(g),
+                           dim3(kStreamThreadsLarge), lds, s, p);
+    else if (large)
+        hipLaunchKernelGGL((step_stream_kernel<false, kStreamThreadsLarge>), dim3(g),
+                           dim3(kStreamThreadsLarge), lds, s, p);
+    else if (vvec)
+        hipLaunchKernelGGL((step_stream_kernel<true, kStreamThreads>), dim3(g),
+                           dim3(kStreamThreads), lds, s, p);
     else
-        hipLaunchKernelGGL((step_stream_kernel<false>), dim3(g), dim3(kStreamThreads), lds, s, p);
+        hipLaunchKernelGGL((step_stream_kernel<false, kStreamThreads>), dim3(g),
+                           dim3(kStreamThreads), lds, s, p);
     e = hipGetLastError();
     if (e == hipSuccess && ev_stop) e = hipEventRecord(ev_stop, s);
     return e;
