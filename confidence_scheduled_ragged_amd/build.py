@@ -2,7 +2,9 @@
 
 Every .hip source under csrc/ is compiled to an object in _build/ (in
 parallel), then linked into confidence_scheduled_ragged_amd/libdspark.so.
-Packed-fp32 instructions are disabled for device code.
+The fused step (fused.hip) is compiled twice: once as is, once with
+DSPARK_SLOTS32=1 (its kernels without 64-bit division, for steps whose slot
+counts fit in 32 bits). Packed-fp32 instructions are disabled for device code.
 """
 import glob
 import os
@@ -28,9 +30,17 @@ def sources():
     return sorted(glob.glob(os.path.join(CSRC, "*.hip")))
 
 
-def _compile(src, verbose):
-    obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [HIPCC, *CFLAGS, "-c", src, "-o", obj]
+def units():
+    """(source, extra flags, object name) of every object in the library."""
+    out = [(src, [], os.path.basename(src) + ".o") for src in sources()]
+    out.append((os.path.join(CSRC, "fused.hip"), ["-DDSPARK_SLOTS32=1"], "fused_slots32.o"))
+    return out
+
+
+def _compile(unit, verbose):
+    src, extra, name = unit
+    obj = os.path.join(BUILD, name)
+    cmd = [HIPCC, *CFLAGS, *extra, "-c", src, "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -46,9 +56,9 @@ def _compile(src, verbose):
 
 def build(verbose: bool = False) -> str:
     os.makedirs(BUILD, exist_ok=True)
-    srcs = sources()
-    with ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
-        objs = list(ex.map(lambda s: _compile(s, verbose), srcs))
+    todo = units()
+    with ThreadPoolExecutor(max_workers=min(8, len(todo))) as ex:
+        objs = list(ex.map(lambda u: _compile(u, verbose), todo))
     tmp = LIB + ".tmp"
     cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     if verbose:

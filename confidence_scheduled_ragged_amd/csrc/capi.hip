@@ -280,10 +280,11 @@ static dspark_status step_launch(const dspark_bf16 *hidden, const dspark_bf16 *w
     float *surv = survival ? survival : reinterpret_cast<float *>(wsb + ws_surv_offset(B, gamma));
     float *cf = conf ? conf : reinterpret_cast<float *>(wsb + ws_conf_offset(B, gamma));
     hipEvent_t es = static_cast<hipEvent_t>(ev_start), et = static_cast<hipEvent_t>(ev_stop);
-    hipError_t e = launch_fused_step(hidden, w, bias, temps, tokens, logits, B, gamma, d, V, mode,
-                                     cutoff, budget, cf, surv, lengths, cu_seqlens, packed_tokens,
-                                     packed_src_row, packed_argmax, accepted, bonus, ws, s, es, et,
-                                     launches, wait_ticks);
+    auto fused = fused_slots_fit_32(B, gamma, V, logits) ? slots32::launch_fused_step
+                                                         : slots64::launch_fused_step;
+    hipError_t e = fused(hidden, w, bias, temps, tokens, logits, B, gamma, d, V, mode, cutoff,
+                         budget, cf, surv, lengths, cu_seqlens, packed_tokens, packed_src_row,
+                         packed_argmax, accepted, bonus, ws, s, es, et, launches, wait_ticks);
     if (e != hipErrorNotSupported) return launched(e);
     // sizes outside the fused kernels' limits: the same step through the stage kernels
     e = launch_confidence(hidden, w, bias, temps, B, gamma, d, cf, surv, s);

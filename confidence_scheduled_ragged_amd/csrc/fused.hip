@@ -50,6 +50,11 @@
 #include "sched_dev.hpp"
 
 namespace dspark {
+#if DSPARK_SLOTS32
+namespace slots32 {
+#else
+namespace slots64 {
+#endif
 
 constexpr int kFrontThreads = 512;
 constexpr int kFusedSelPer = 8;  // survival values per thread of the in-front select
@@ -1128,4 +1133,5 @@ hipError_t launch_fused_step(const uint16_t *hidden, const uint16_t *w, float bi
     return e;
 }
 
+}  // namespace slots32 / slots64
 }  // namespace dspark

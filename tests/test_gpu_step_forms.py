@@ -75,6 +75,10 @@ CASES = {
     # the full static block at full size: in two launches every sub-chunk is
     # long (about 19 000 slots), two loads deep
     "static_full": CONFIGS["mixed_threshold"].scaled(mode="static"),
+    # draft slots past 2^32 (4 x 16 rows of an odd vocabulary of 70 000 001,
+    # one slot per logit on the scalar path): the slot arithmetic of both forms
+    # takes its wide division path
+    "wide_slots": CONFIGS["tiny"].scaled(B=4, gamma=16, d=64, V=70_000_001, cutoff=0.0),
     # batch-wide picks (two launches under either setting): B*gamma = 4096
     # positions, the most the in-kernel pick takes; d = 7168 reads a 14 KiB
     # head; odd d and V take the scalar paths; a batch over 4096 positions
