@@ -79,6 +79,10 @@ CASES = {
     # one slot per logit on the scalar path): the slot arithmetic of both forms
     # takes its wide division path
     "wide_slots": CONFIGS["tiny"].scaled(B=4, gamma=16, d=64, V=70_000_001, cutoff=0.0),
+    # the same past 2^32 under a batch budget (T = 62 of 64 positions: the
+    # front's pick, then 62 draft rows, 4.3e9 slots)
+    "wide_slots_budget": CONFIGS["tiny"].scaled(B=4, gamma=16, d=64, V=70_000_001, mode="budget",
+                                                budget_per_request=15.5),
     # batch-wide picks (two launches under either setting): B*gamma = 4096
     # positions, the most the in-kernel pick takes; d = 7168 reads a 14 KiB
     # head; odd d and V take the scalar paths; a batch over 4096 positions
